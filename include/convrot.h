@@ -1,0 +1,150 @@
+/*
+ * convrot.h -- C ABI of libconvrot.so, the INT8 ConvRot linear layer for
+ * AMD MI355X (gfx950).
+ *
+ * What the layer computes (page "int8 Compute", InvokeAI docs, opening
+ * section): the weight is an int8_tensorwise build (int8 values plus one
+ * scale) quantized after a rotation; each call rotates its input with the
+ * same rotation, quantizes it to int8 per token and multiplies int8 by int8.
+ * The rotation is group-wise (same page, "What stays on the default path":
+ * groups of 256 in every published build; the synthetic workloads here also
+ * use 128) and is applied block after block along K (page "Explanation of
+ * INT8 ConvRot", "What is INT8 ConvRot?").  Outputs are bf16 (same page
+ * "int8 Compute", "What stays on the default path": BF16/FP16 compute).
+ *
+ * Definitions used by every entry point (the readings of what the pages
+ * leave open):
+ *   R   = blockdiag(H_g / sqrt(g)) along K, H_g the Sylvester Hadamard matrix
+ *         (H[i][j] = (-1)^popcount(i & j)); applied in fp32 as the radix-2
+ *         butterfly with half-span h = 1, 2, ..., g/2 ((a, b) -> (a+b, a-b)),
+ *         then one multiply by the float nearest to 1/sqrt(g).
+ *   s_w = max |W R| / 127 over the whole weight;   Wq = rne(W R / s_w)
+ *   s_x = max_k |x_m R| / 127 per token m;         q_x = rne(x_m R / s_x)
+ *         (IEEE fp32 division, round half to even, clamp to [-127, 127];
+ *          an all-zero token or weight gets scale 0 and codes 0)
+ *   acc = q_x . Wq^T in int32 (exact)
+ *   y   = bf16_rne(fmaf((float)acc, s_x[m] * s_w, bias[n]))   (bias 0 if NULL)
+ * Results are bit-identical from run to run and do not depend on how the
+ * tokens are sliced or tiled (page "int8 Compute": each path is bit-identical
+ * from run to run; streamed and resident runs give the same image).
+ *
+ * Conventions for every entry point
+ *   - All tensors are row-major and contiguous; bf16 values are raw 16-bit
+ *     patterns.  Every pointer argument except `stream` (and the host pointer
+ *     noted at convrot_last_error) is a DEVICE pointer on the current HIP
+ *     device.  The caller owns every buffer; the library never allocates,
+ *     frees or keeps a pointer after the call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every launch is asynchronous on that stream; no entry point waits for
+ *     the device.  Outputs are valid once the stream has reached the call.
+ *   - Argument errors are found before any launch and return a negative
+ *     status without touching the device; convrot_last_error() then holds a
+ *     message.  A failed launch returns CONVROT_EHIP.  Faults inside a kernel
+ *     surface at the caller's next synchronisation and are not recoverable.
+ *   - Group sizes: 128 or 256 (else CONVROT_EUNSUPPORTED).  K must be a
+ *     multiple of the group and at most 131072 (so 127*127*K < 2^31).
+ *     M = 0 is a valid empty batch (nothing is launched); N >= 1.
+ *   - x, xq, wq, y and workspace must be 16-byte aligned (CONVROT_EALIGN).
+ *   - No entry point falls back to another implementation: an unsupported
+ *     request is an error.
+ */
+#ifndef CONVROT_H
+#define CONVROT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CONVROT_ABI_VERSION 1
+
+enum convrot_status {
+    CONVROT_OK = 0,
+    CONVROT_EINVAL = -1,        /* bad size, NULL pointer, K % group != 0, ... */
+    CONVROT_EUNSUPPORTED = -2,  /* group not in {128, 256}, unknown dtype     */
+    CONVROT_EALIGN = -3,        /* a pointer is not 16-byte aligned           */
+    CONVROT_EWORKSPACE = -4,    /* workspace missing or too small             */
+    CONVROT_EHIP = -5           /* a HIP launch or query failed               */
+};
+
+enum convrot_dtype { CONVROT_F32 = 0, CONVROT_BF16 = 1 };
+
+/* CONVROT_ABI_VERSION of the built library. */
+int convrot_abi_version(void);
+
+/* Message of the last failed call on this thread (host pointer to static,
+ * thread-local storage; "" if none).  Valid until the next call. */
+const char *convrot_last_error(void);
+
+/* ---------------------------------------------------------------- weights */
+
+/* Workspace bytes convrot_prepare_weight needs (a few bytes for the global
+ * absmax; the same for every shape). */
+size_t convrot_prepare_weight_workspace(int64_t N, int64_t K);
+
+/* Offline weight preparation (page "int8 Compute": builds ship the weight
+ * already rotated and int8_tensorwise quantized; this makes such a build
+ * from a float weight).
+ *   w           [N, K] weight, fp32 (w_dtype CONVROT_F32) or bf16 (CONVROT_BF16),
+ *               PyTorch nn.Linear layout (out x in, K contiguous).
+ *   wq_out      [N, K] int8 codes of W R.
+ *   w_scale_out one float on the device: s_w.
+ *   workspace   >= convrot_prepare_weight_workspace(N, K) bytes, device.
+ * Two passes over w (rotate + global absmax, then rotate + quantize). */
+int convrot_prepare_weight(const void *w, int w_dtype, int64_t N, int64_t K, int group,
+                           int8_t *wq_out, float *w_scale_out,
+                           void *workspace, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- forward */
+
+/* Workspace bytes convrot_linear needs: codes and scales of one slice of
+ * min(M, 2N) tokens (page "int8 Compute", "Memory": the input is quantized in
+ * slices of at most twice the output width, so the working memory never
+ * exceeds the 2*N*K bytes of the unpacked bf16 weight). */
+size_t convrot_linear_workspace(int64_t M, int64_t K, int64_t N);
+
+/* The whole layer: y = dequant(rotate_quant(x) . Wq^T) + bias.
+ *   x_bf16    [M, K] bf16 activation.
+ *   wq        [N, K] int8 and w_scale (one float, device) from
+ *             convrot_prepare_weight with the same group.
+ *   bias_bf16 [N] bf16 or NULL.
+ *   y_bf16    [M, N] bf16 output (must not overlap the inputs).
+ *   workspace ws_bytes of device scratch.  Tokens are processed in slices of
+ *             S = min(M, 2N, ws_bytes / (K + 4) rounded down to a multiple
+ *             of 16 (or M if smaller)) rows; a workspace too small for one
+ *             16-row slice (or for M rows if M < 16) is CONVROT_EWORKSPACE.
+ *             The result does not depend on S.
+ * Per slice: one rotate+quant launch, then one GEMM+epilogue launch. */
+int convrot_linear(const void *x_bf16, int64_t M, int64_t K,
+                   const int8_t *wq, const float *w_scale, int64_t N, int group,
+                   const void *bias_bf16, void *y_bf16,
+                   void *workspace, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- stages
+ * The same kernels convrot_linear launches, exposed one by one. */
+
+/* Rotate + per-token quantization: xq [M, K] int8, x_scale [M] fp32. */
+int convrot_rotate_quant(const void *x_bf16, int64_t M, int64_t K, int group,
+                         int8_t *xq, float *x_scale, void *stream);
+
+/* Raw int32 products acc [M, N] = xq . wq^T (xq [M, K], wq [N, K] int8).
+ * Runs the GEMM main loop of convrot_gemm_dequant with an int32 store in
+ * place of the epilogue.  K a multiple of 128, at most 131072. */
+int convrot_gemm_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,
+                     int32_t *acc, void *stream);
+
+/* GEMM + fused epilogue: y [M, N] bf16 = bf16_rne(fmaf((float)(xq . wq^T),
+ * x_scale[m] * w_scale[0], bias[n])).  x_scale [M] and w_scale [1] are
+ * device fp32; bias_bf16 [N] or NULL.  K a multiple of 128, at most 131072. */
+int convrot_gemm_dequant(const int8_t *xq, const float *x_scale,
+                         const int8_t *wq, const float *w_scale,
+                         const void *bias_bf16, void *y_bf16,
+                         int64_t M, int64_t N, int64_t K, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVROT_H */

@@ -1,0 +1,230 @@
+/*
+ * convrot_oracle.c -- CPU oracle for the INT8 ConvRot linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY (see convrot_oracle.h).  Plain scalar C99, one
+ * thread, no intrinsics, no blocking or fusion.  Build it with
+ *   gcc -O2 -std=c99 -ffp-contract=off -fno-fast-math -fPIC -shared
+ * so that every float operation below is one IEEE binary32 operation in
+ * round-to-nearest-even, in the order written.
+ *
+ * Sources of each step:
+ *  - page "int8 Compute" (InvokeAI docs), opening section: the layer rotates
+ *    and quantizes its input to int8 per token and multiplies int8 by int8;
+ *    weights are an int8_tensorwise build (int8 values + one scale).
+ *  - same page, "What stays on the default path": rotation is done in
+ *    groups (256 in every published build); without it one outlier channel
+ *    sets the scale of a whole token.
+ *  - page "Explanation of INT8 ConvRot", "What is INT8 ConvRot?": group-wise
+ *    rotation applied block by block, like a convolution.
+ *  - page "int8 Compute", "What stays on the default path": compute is BF16
+ *    (outputs are bf16 here).
+ * The matrix, rounding and scale formulas the pages leave open are the
+ * readings stated in convrot_oracle.h.
+ */
+#include "convrot_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+static int is_pow2(int g) { return g >= 1 && (g & (g - 1)) == 0; }
+
+float oracle_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)
+        return 0x7fc0; /* NaN (never produced on the tested path) */
+    /* round to nearest, ties to even, on the 16 dropped bits */
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+float oracle_rot_scale(int g)
+{
+    return (float)(1.0 / sqrt((double)g));
+}
+
+/* O1.  Sylvester Hadamard: H[i][j] = (-1)^popcount(i & j). */
+int oracle_hadamard(int g, int32_t *H)
+{
+    if (!is_pow2(g) || H == NULL) return -1;
+    for (int i = 0; i < g; ++i) {
+        for (int j = 0; j < g; ++j) {
+            int bits = i & j, parity = 0;
+            while (bits) { parity ^= bits & 1; bits >>= 1; }
+            H[(int64_t)i * g + j] = parity ? -1 : 1;
+        }
+    }
+    return 0;
+}
+
+/* O2 on one block of g floats: butterfly with half-span h ascending, then
+ * the normalisation multiply.  H_g v equals this butterfly because the
+ * Sylvester matrix factors as a product of one (a+b, a-b) stage per bit of
+ * the index. */
+static void rotate_block(float *v, int g, float c)
+{
+    for (int h = 1; h < g; h <<= 1) {
+        for (int i = 0; i < g; i += 2 * h) {
+            for (int j = i; j < i + h; ++j) {
+                float a = v[j];
+                float b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+        }
+    }
+    for (int j = 0; j < g; ++j) v[j] = v[j] * c;
+}
+
+int oracle_rotate_rows(float *v, int64_t rows, int64_t K, int g)
+{
+    if (!is_pow2(g) || rows < 0 || K < 0 || (K % g) != 0 || (rows > 0 && K > 0 && v == NULL))
+        return -1;
+    float c = oracle_rot_scale(g);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < K; b += g)
+            rotate_block(v + r * K + b, g, c);
+    return 0;
+}
+
+/* Symmetric int8 code of v under scale s: clamp(rne(v / s), -127, 127).
+ * nearbyintf rounds half to even in the default rounding mode. */
+static int8_t quant_code(float v, float s)
+{
+    if (s == 0.0f) return 0;
+    float r = nearbyintf(v / s);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    return (int8_t)r;
+}
+
+/* O3.  Tensorwise: one absmax over the whole rotated weight. */
+int oracle_quant_weight(const float *w, int64_t N, int64_t K, int g,
+                        int8_t *wq, float *s_w, float *w_rot)
+{
+    if (!is_pow2(g) || N < 1 || K < 1 || (K % g) != 0 || w == NULL || wq == NULL || s_w == NULL)
+        return -1;
+    float *rot = w_rot ? w_rot : (float *)malloc((size_t)(N * K) * sizeof(float));
+    if (rot == NULL) return -3;
+    memcpy(rot, w, (size_t)(N * K) * sizeof(float));
+    oracle_rotate_rows(rot, N, K, g);
+
+    float amax = 0.0f;
+    for (int64_t i = 0; i < N * K; ++i) {
+        float a = fabsf(rot[i]);
+        if (a > amax) amax = a;
+    }
+    float s = amax / 127.0f;
+    for (int64_t i = 0; i < N * K; ++i) wq[i] = quant_code(rot[i], s);
+    *s_w = s;
+    if (rot != w_rot) free(rot);
+    return 0;
+}
+
+/* O4 for one token row: widen bf16 -> fp32, rotate, absmax, scale, codes. */
+static void quant_act_row(const uint16_t *xrow, int64_t K, int g, float *rot,
+                          int8_t *qrow, float *srow)
+{
+    for (int64_t k = 0; k < K; ++k) rot[k] = oracle_bf16_to_f32(xrow[k]);
+    oracle_rotate_rows(rot, 1, K, g);
+    float amax = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        float a = fabsf(rot[k]);
+        if (a > amax) amax = a;
+    }
+    float s = amax / 127.0f;
+    for (int64_t k = 0; k < K; ++k) qrow[k] = quant_code(rot[k], s);
+    *srow = s;
+}
+
+int oracle_quant_act(const uint16_t *x, int64_t M, int64_t K, int g,
+                     int8_t *q, float *s, float *x_rot)
+{
+    if (!is_pow2(g) || M < 0 || K < 1 || (K % g) != 0 || (M > 0 && (x == NULL || q == NULL || s == NULL)))
+        return -1;
+    float *rot = (float *)malloc((size_t)K * sizeof(float));
+    if (rot == NULL) return -3;
+    for (int64_t m = 0; m < M; ++m) {
+        quant_act_row(x + m * K, K, g, rot, q + m * K, s + m);
+        if (x_rot) memcpy(x_rot + m * K, rot, (size_t)K * sizeof(float));
+    }
+    free(rot);
+    return 0;
+}
+
+/* O5.  Exact integer dot products; int64 accumulation, then a range check. */
+int oracle_gemm_i32(const int8_t *a, const int8_t *b, int64_t M, int64_t N,
+                    int64_t K, int32_t *acc)
+{
+    if (M < 0 || N < 0 || K < 0 || ((M > 0 && N > 0) && (a == NULL || b == NULL || acc == NULL)))
+        return -1;
+    int rc = 0;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t sum = 0;
+            for (int64_t k = 0; k < K; ++k)
+                sum += (int64_t)a[m * K + k] * (int64_t)b[n * K + k];
+            if (sum > INT32_MAX || sum < INT32_MIN) rc = -2;
+            acc[m * N + n] = (int32_t)sum;
+        }
+    }
+    return rc;
+}
+
+/* O6.  alpha = s_x[m] * s_w first, then one fused multiply-add with the
+ * bias, then one rounding to bf16. */
+int oracle_epilogue(const int32_t *acc, const float *s_x, float s_w,
+                    const uint16_t *bias, int64_t M, int64_t N, uint16_t *y)
+{
+    if (M < 0 || N < 0 || ((M > 0 && N > 0) && (acc == NULL || s_x == NULL || y == NULL)))
+        return -1;
+    for (int64_t m = 0; m < M; ++m) {
+        float alpha = s_x[m] * s_w;
+        for (int64_t n = 0; n < N; ++n) {
+            float bn = bias ? oracle_bf16_to_f32(bias[n]) : 0.0f;
+            float v = fmaf((float)acc[m * N + n], alpha, bn);
+            y[m * N + n] = oracle_f32_to_bf16(v);
+        }
+    }
+    return 0;
+}
+
+int oracle_linear_rows(const uint16_t *x, int64_t M, int64_t K,
+                       const int64_t *rows, int64_t R,
+                       const int8_t *wq, float s_w, int64_t N, int g,
+                       const uint16_t *bias, uint16_t *y,
+                       int8_t *q_rows, float *s_rows)
+{
+    if (!is_pow2(g) || M < 1 || K < 1 || N < 1 || R < 0 || (K % g) != 0 ||
+        x == NULL || wq == NULL || y == NULL || (R > 0 && rows == NULL))
+        return -1;
+    for (int64_t r = 0; r < R; ++r)
+        if (rows[r] < 0 || rows[r] >= M) return -1;
+
+    float *rot = (float *)malloc((size_t)K * sizeof(float));
+    int8_t *q = (int8_t *)malloc((size_t)K);
+    int32_t *acc = (int32_t *)malloc((size_t)N * sizeof(int32_t));
+    if (!rot || !q || !acc) { free(rot); free(q); free(acc); return -3; }
+
+    int rc = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        float s;
+        quant_act_row(x + rows[r] * K, K, g, rot, q, &s);
+        if (oracle_gemm_i32(q, wq, 1, N, K, acc) != 0) rc = -2;
+        oracle_epilogue(acc, &s, s_w, bias, 1, N, y + r * N);
+        if (q_rows) memcpy(q_rows + r * K, q, (size_t)K);
+        if (s_rows) s_rows[r] = s;
+    }
+    free(rot); free(q); free(acc);
+    return rc;
+}

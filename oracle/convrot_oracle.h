@@ -1,0 +1,92 @@
+/*
+ * convrot_oracle.h -- CPU oracle for the INT8 ConvRot linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is a plain, slow, single-threaded C99
+ * restatement of what the layer computes.  Only the test-suite, the smoke
+ * check and the CPU-baseline leg of the benchmark may load it.  It shares no
+ * code, header, table or constant with the HIP library.
+ *
+ * Method (page "int8 Compute", InvokeAI docs, opening section): each ConvRot
+ * layer rotates its input, quantizes it to int8 per token, and multiplies int8
+ * by int8; the weight is an int8_tensorwise build (int8 values plus one
+ * scale).  The rotation works in groups (same page, "What stays on the default
+ * path": published builds use groups of 256) and is the same orthogonal block
+ * rotation on both operands, so x.W^T = (xR).(WR)^T (page "Explanation of INT8
+ * ConvRot", section "What is INT8 ConvRot?": rotation applied group by group,
+ * block after block, like a convolution).
+ *
+ * Readings where the pages are silent (each one is listed with its reason in
+ * the design notes of the repository):
+ *   R  = blockdiag(H_g / sqrt(g)), H_g the Sylvester Hadamard matrix,
+ *        H[i][j] = (-1)^popcount(i & j).
+ *   rotation in fp32: radix-2 butterfly with ascending half-span h = 1,2,..,g/2,
+ *        pair (a,b) -> (a+b, a-b), then one multiply by c_g, the float nearest
+ *        to 1/sqrt(g).
+ *   scales: s = absmax / 127 (fp32, IEEE division); codes q = clamp(rne(v/s),
+ *        -127, 127); an all-zero row/tensor gives s = 0 and codes 0.
+ *   epilogue: y = bf16_rne(fmaf((float)acc, s_x[m]*s_w, bias[n])).
+ *
+ * All arrays are row-major and contiguous.  bf16 values travel as their raw
+ * uint16 bit patterns.  Functions return 0 on success and a negative value on
+ * a bad argument (nothing is written in that case).
+ */
+#ifndef CONVROT_ORACLE_H
+#define CONVROT_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* float <-> bf16 bit conversions (widening is exact; narrowing is RNE). */
+float    oracle_bf16_to_f32(uint16_t b);
+uint16_t oracle_f32_to_bf16(float f);
+
+/* c_g: the float nearest to 1/sqrt(g). */
+float oracle_rot_scale(int g);
+
+/* O1: the g x g Sylvester Hadamard matrix as +-1 integers.  g a power of 2. */
+int oracle_hadamard(int g, int32_t *H);
+
+/* O2: rotate every length-g block of each row of v (rows x K, fp32) in place.
+ * g is a power of two (g = 1 is the identity rotation) and divides K. */
+int oracle_rotate_rows(float *v, int64_t rows, int64_t K, int g);
+
+/* O3: tensorwise weight quantization.  w: fp32 [N, K] (not modified).
+ * wq: int8 [N, K]; *s_w: the single scale.  w_rot (nullable): fp32 [N, K]
+ * receives the rotated weight. */
+int oracle_quant_weight(const float *w, int64_t N, int64_t K, int g,
+                        int8_t *wq, float *s_w, float *w_rot);
+
+/* O4: per-token activation quantization.  x: bf16 bits [M, K].
+ * q: int8 [M, K]; s: fp32 [M].  x_rot (nullable): fp32 [M, K]. */
+int oracle_quant_act(const uint16_t *x, int64_t M, int64_t K, int g,
+                     int8_t *q, float *s, float *x_rot);
+
+/* O5: acc[m][n] = sum_k a[m][k] * b[n][k], accumulated in int64.
+ * Returns -2 if a result does not fit int32. */
+int oracle_gemm_i32(const int8_t *a, const int8_t *b, int64_t M, int64_t N,
+                    int64_t K, int32_t *acc);
+
+/* O6: y[m][n] = bf16_rne(fmaf((float)acc[m][n], s_x[m]*s_w, bias[n])).
+ * bias: bf16 bits [N] or NULL (then +0.0f). */
+int oracle_epilogue(const int32_t *acc, const float *s_x, float s_w,
+                    const uint16_t *bias, int64_t M, int64_t N, uint16_t *y);
+
+/* O4 -> O5 -> O6 for the rows of x listed in rows[0..R) (R rows, each index
+ * in [0, M)).  Output y: bf16 bits [R, N]; q_rows: int8 [R, K] and s_rows:
+ * fp32 [R] (both nullable) receive the rows' codes and scales.  wq/s_w come
+ * from oracle_quant_weight.  This is the whole layer, evaluated on a subset
+ * of tokens, which is exact because every token is quantized on its own. */
+int oracle_linear_rows(const uint16_t *x, int64_t M, int64_t K,
+                       const int64_t *rows, int64_t R,
+                       const int8_t *wq, float s_w, int64_t N, int g,
+                       const uint16_t *bias, uint16_t *y,
+                       int8_t *q_rows, float *s_rows);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVROT_ORACLE_H */

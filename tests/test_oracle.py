@@ -1,0 +1,427 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test ties one oracle step (O1..O6) to something other than the oracle
+itself: a textbook matrix, a closed form, an invariant, brute force in exact
+integer / rational arithmetic, or a library routine that a special case
+reduces to.  Together they are chosen so that a plausible slip (a dropped
+term, a wrong sign or index, a transposed operand, a wrong scale or rounding
+mode) fails at least one of them.
+"""
+from fractions import Fraction
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from w8a8_rotated_int8_convrot_amd import synth
+
+GROUPS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+
+
+def read_facts(golden_dir):
+    facts = {}
+    with open(os.path.join(golden_dir, "pages_facts.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].split()
+            if line:
+                facts[line[0]] = float(line[1])
+    return facts
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def bits(x):
+    return synth.to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+# ---------------------------------------------------------------- O1 Hadamard
+
+def test_hadamard_matches_textbook_h8(golden_dir):
+    H8 = np.loadtxt(os.path.join(golden_dir, "sylvester_h8.txt"), dtype=np.int32)
+    assert np.array_equal(oracle.hadamard(8), H8)
+
+
+@pytest.mark.parametrize("g", GROUPS)
+def test_hadamard_identity_and_library(g):
+    H = oracle.hadamard(g).astype(np.int64)
+    assert np.array_equal(H @ H.T, g * np.eye(g, dtype=np.int64))       # H H^T = g I
+    assert np.array_equal(H, H.T)                                         # symmetric
+    assert np.all(H[0] == 1) and np.all(H[:, 0] == 1)
+    assert np.array_equal(H, scipy.linalg.hadamard(g))                    # Sylvester construction
+
+
+@pytest.mark.parametrize("g", GROUPS)
+def test_rotation_scale_is_nearest_float(g):
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    exact = Decimal(1) / Decimal(g).sqrt()
+    c = oracle.rot_scale(g)
+    lo, hi = np.nextafter(c, np.float32(0)), np.nextafter(c, np.float32(1))
+    err = abs(Decimal(float(c)) - exact)
+    assert err <= abs(Decimal(float(lo)) - exact) and err <= abs(Decimal(float(hi)) - exact)
+
+
+@pytest.mark.parametrize("g", (128, 256))
+def test_block_rotation_is_orthogonal(g):
+    K = 4 * g
+    c = float(oracle.rot_scale(g))
+    R = np.kron(np.eye(K // g), oracle.hadamard(g).astype(np.float64) * c)
+    assert np.max(np.abs(R @ R.T - np.eye(K))) <= 1e-6
+
+
+# ---------------------------------------------------------------- O2 rotation
+
+@pytest.mark.parametrize("g", GROUPS)
+def test_rotation_brute_force_within_bound(g):
+    K = 4 * max(g, 8)
+    v = rng(g).standard_normal((5, K)).astype(np.float32)
+    got = oracle.rotate(v, g).astype(np.float64)
+    c = float(oracle.rot_scale(g))
+    H = oracle.hadamard(g).astype(np.float64)
+    u = 2.0 ** -24
+    for r in range(v.shape[0]):
+        for b in range(0, K, g):
+            blk = v[r, b:b + g].astype(np.float64)
+            exact = (H @ blk) * (1.0 / np.sqrt(g))
+            # log2(g) rounded additions on sums bounded by sum|v|, the rounded
+            # scale constant and the final multiply.
+            bound = (np.log2(g) * u * np.sum(np.abs(blk)) * c + 2 * u * np.abs(exact)
+                     + u * np.sum(np.abs(blk)) * c + 1e-30)
+            assert np.all(np.abs(got[r, b:b + g] - exact) <= bound)
+
+
+@pytest.mark.parametrize("g", (4, 16, 64, 256))
+def test_rotation_is_an_involution_on_small_integers(g):
+    # c_g = 2^-log2(g)/2 is exact for these g, so R R v = v exactly.
+    v = rng(7).integers(-50, 51, size=(3, 2 * g)).astype(np.float32)
+    assert np.array_equal(oracle.rotate(oracle.rotate(v, g), g), v)
+
+
+@pytest.mark.parametrize("g", (8, 128, 256))
+def test_rotation_of_one_hot_is_a_scaled_hadamard_row(g):
+    H = oracle.hadamard(g)
+    c = oracle.rot_scale(g)
+    K = 2 * g
+    for j in (0, 1, g // 2 + 3, g - 1):
+        e = np.zeros(K, np.float32)
+        e[g + j] = 1.0                      # second block
+        got = oracle.rotate(e, g)
+        assert np.all(got[:g] == 0)
+        assert np.array_equal(got[g:], (H[j] * c).astype(np.float32))
+
+
+def test_rotation_acts_per_block_and_per_row():
+    g = 128
+    v = rng(3).standard_normal((4, 3 * g)).astype(np.float32)
+    full = oracle.rotate(v, g)
+    for r in range(4):
+        for b in range(3):
+            assert np.array_equal(full[r, b * g:(b + 1) * g], oracle.rotate(v[r, b * g:(b + 1) * g], g))
+
+
+# ---------------------------------------------------------------- O3/O4 quantizers
+
+def rtn_reference(v):
+    """Plain symmetric per-row round-to-nearest-even int8 (textbook RTN)."""
+    v = np.asarray(v, np.float32)
+    s = (np.max(np.abs(v), axis=-1) / np.float32(127)).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        q = np.rint(v / s[..., None])
+    q = np.where(s[..., None] == 0, 0, np.clip(q, -127, 127))
+    return q.astype(np.int8), s
+
+
+def test_identity_rotation_reduces_to_textbook_rtn():
+    x = bits(rng(11).standard_normal((9, 64)) * 3)
+    x[4] = 0                                                   # a zero token
+    q, s = oracle.quant_act(x, 1)
+    q_ref, s_ref = rtn_reference(oracle.bf16_bits_to_f32(x))
+    assert np.array_equal(q, q_ref) and np.array_equal(s, s_ref)
+
+    w = (rng(12).standard_normal((5, 64)) * 0.02).astype(np.float32)
+    wq, s_w = oracle.quant_weight(w, 1)
+    wq_ref, s_ref = rtn_reference(w.reshape(1, -1))
+    assert np.array_equal(wq, wq_ref.reshape(5, 64)) and s_w == s_ref[0]
+
+
+def test_hand_worked_rtn_example():
+    # g = 1, row [1, -2, 0.5, 4]: absmax 4, s = RN(4/127); the quotients are
+    # 31.75, -63.5, 15.875, 127 up to one rounding, -63.5 is an exact tie in
+    # float32 (checked in exact rationals below) and rounds to the even -64.
+    x = bits([[1.0, -2.0, 0.5, 4.0]])
+    q, s = oracle.quant_act(x, 1)
+    s_exact = Fraction(float(np.float32(4.0) / np.float32(127.0)))
+    assert s[0] == np.float32(4.0 / 127.0)
+    assert abs(Fraction(2) / s_exact - Fraction(127, 2)) < Fraction(1, 2 ** 19)
+    assert q.tolist() == [[32, -64, 16, 127]]
+
+
+@pytest.mark.parametrize("g", (128, 256))
+def test_one_hot_token_closed_form(g):
+    K = 2 * g
+    for j, mag in ((5, 1.0), (g - 1, 8.0), (0, 0.25)):
+        x = np.zeros((1, K), np.float32)
+        x[0, j] = -mag
+        q, s = oracle.quant_act(bits(x), g)
+        H = oracle.hadamard(g)
+        assert np.array_equal(q[0, :g], (-127 * H[j]).astype(np.int8))
+        assert np.all(q[0, g:] == 0)
+        assert s[0] == np.float32(np.float32(mag) * oracle.rot_scale(g)) / np.float32(127)
+
+
+def exactly_representable_codes(g, blocks, seed):
+    """Integer codes q' per block with max|q'| = 127 and sum|q'| <= 256, and
+    x = H_g q' per block (integers of magnitude <= 256: exact in bf16)."""
+    r = rng(seed)
+    qp = np.zeros(blocks * g, np.int64)
+    H = oracle.hadamard(g).astype(np.int64)
+    for b in range(blocks):
+        idx = r.choice(g, size=6, replace=False)
+        vals = r.integers(-25, 26, size=6)
+        vals[0] = 127 if r.random() < 0.5 else -127
+        qp[b * g + idx] = vals
+    x = np.concatenate([H @ qp[b * g:(b + 1) * g] for b in range(blocks)])
+    assert np.max(np.abs(x)) <= 256
+    return qp, x.astype(np.float32)
+
+
+@pytest.mark.parametrize("g", (128, 256))
+def test_exactly_representable_inputs_quantize_without_error(g):
+    qp, x = exactly_representable_codes(g, 3, seed=g)
+    q, s, rot = oracle.quant_act(bits(x[None, :]), g, return_rot=True)
+    assert np.array_equal(q[0], qp.astype(np.int8))
+    # the dequantized activation equals the rotated one up to the rounding of s
+    deq = s[0].astype(np.float64) * q[0]
+    assert np.max(np.abs(deq - rot[0]) / np.maximum(np.abs(rot[0]), 1e-30)) <= 4e-7
+    wq, s_w = oracle.quant_weight(x[None, :], g)
+    assert np.array_equal(wq[0], qp.astype(np.int8))
+
+
+@pytest.mark.parametrize("g", (128, 256))
+def test_quantization_error_shrinks_to_zero_near_representable_inputs(g):
+    qp, x = exactly_representable_codes(g, 2, seed=3 * g)
+    N = 4
+    W = np.stack([exactly_representable_codes(g, 2, seed=5 * g + i)[1] for i in range(N)])
+    noise = rng(1).standard_normal(x.shape).astype(np.float32)
+    errs = []
+    for delta in (2.0, 0.5, 0.125, 0.0):
+        xb = bits((x + delta * noise)[None, :])
+        wq, s_w = oracle.quant_weight(W, g)
+        y, _, _ = oracle.linear(xb, wq, s_w, g)
+        ref = oracle.reference_fp64(xb, W)
+        errs.append(oracle.nrmse(oracle.bf16_bits_to_f32(y), ref))
+    assert errs[0] > errs[-1] and errs[1] > errs[-1]
+    assert errs[-1] <= 2.0 ** -8          # only the bf16 output rounding is left
+
+
+@pytest.mark.parametrize("g", (128, 256))
+def test_quantizer_invariants(g):
+    x = rng(21).standard_normal((6, 3 * g)).astype(np.float32) * 2
+    x[2, 17] = 60.0                                   # an outlier channel
+    xb = bits(x)
+    q, s, rot = oracle.quant_act(xb, g, return_rot=True)
+    # scale by powers of two
+    for e in (-3, 4):
+        q2, s2 = oracle.quant_act(bits(oracle.bf16_bits_to_f32(xb) * np.float32(2.0 ** e)), g)
+        assert np.array_equal(q2, q) and np.array_equal(s2, s * np.float32(2.0 ** e))
+    # sign
+    qn, sn = oracle.quant_act(xb ^ np.uint16(0x8000), g)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    # per-token independence
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    qp, sp = oracle.quant_act(xb[perm], g)
+    assert np.array_equal(qp, q[perm]) and np.array_equal(sp, s[perm])
+    # bounds and the half-step error bound
+    assert np.max(np.abs(q.astype(np.int32))) <= 127
+    assert np.all(np.max(np.abs(q.astype(np.int32)), axis=1) == 127)
+    assert np.all(np.abs(rot / s[:, None].astype(np.float64) - q) <= 0.5 + 1e-5)
+
+
+def test_zero_token_and_zero_weight():
+    g = 128
+    q, s = oracle.quant_act(np.zeros((2, 256), np.uint16), g)
+    assert np.all(q == 0) and np.all(s == 0)
+    wq, s_w = oracle.quant_weight(np.zeros((3, 256), np.float32), g)
+    assert np.all(wq == 0) and s_w == 0
+    # y = bias when the token is zero
+    bias = bits(rng(2).standard_normal(3))
+    y, _, _ = oracle.linear(np.zeros((2, 256), np.uint16), wq, s_w, g, bias)
+    assert np.array_equal(y, np.stack([bias, bias]))
+
+
+def test_weight_scale_is_tensorwise():
+    g = 128
+    w = (rng(5).standard_normal((4, 256)) * 0.02).astype(np.float32)
+    w[2] *= 10.0                                      # one row much larger
+    wq, s_w, rot = oracle.quant_weight(w, g, return_rot=True)
+    assert s_w == np.float32(np.max(np.abs(rot))) / np.float32(127)
+    assert np.max(np.abs(wq[2].astype(np.int32))) == 127
+    assert np.max(np.abs(wq[0].astype(np.int32))) < 40  # small rows use few levels
+    assert np.array_equal(rot, oracle.rotate(w, g))
+
+
+# ---------------------------------------------------------------- O5 GEMM
+
+def test_gemm_brute_force_python_ints():
+    r = rng(8)
+    a = r.integers(-127, 128, size=(3, 7)).astype(np.int8)
+    b = r.integers(-127, 128, size=(4, 7)).astype(np.int8)
+    got = oracle.gemm_i32(a, b)
+    for m in range(3):
+        for n in range(4):
+            assert got[m, n] == sum(int(a[m, k]) * int(b[n, k]) for k in range(7))
+
+
+def test_gemm_random_shapes_against_int64_matmul():
+    r = rng(9)
+    for _ in range(6):
+        M, N, K = (int(v) for v in r.integers(1, 300, size=3))
+        a = r.integers(-127, 128, size=(M, K)).astype(np.int8)
+        b = r.integers(-127, 128, size=(N, K)).astype(np.int8)
+        assert np.array_equal(oracle.gemm_i32(a, b), a.astype(np.int64) @ b.astype(np.int64).T)
+
+
+def test_gemm_extremes_and_overflow():
+    K = 131072
+    a = np.full((1, K), -127, np.int8)
+    b = np.full((2, K), 127, np.int8)
+    b[1] = -127
+    assert oracle.gemm_i32(a, b).tolist() == [[-127 * 127 * K, 127 * 127 * K]]
+    with pytest.raises(OverflowError):
+        oracle.gemm_i32(np.full((1, 140000), 127, np.int8), np.full((1, 140000), 127, np.int8))
+
+
+# ---------------------------------------------------------------- O6 epilogue
+
+def rn_float32(q: Fraction) -> Fraction:
+    """Exact round-to-nearest-even of a rational to binary32 (normal range)."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (e - 23)
+    m = a / ulp
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * ulp
+
+
+def test_bf16_rounding_table(golden_dir):
+    with open(os.path.join(golden_dir, "bf16_rne.txt")) as f:
+        rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    for val, hexbits in rows:
+        assert oracle.f32_to_bf16_bits(float(val)) == int(hexbits, 16), val
+
+
+def test_bf16_rounding_matches_torch():
+    v = np.concatenate([rng(4).standard_normal(20000).astype(np.float32) * 100,
+                        (1 + np.arange(512, dtype=np.float32) * np.float32(2 ** -9))])
+    mine = np.array([oracle.f32_to_bf16_bits(f) for f in v], dtype=np.uint16)
+    assert np.array_equal(mine, synth.to_bf16_bits(v))
+
+
+def test_epilogue_single_rounding_against_exact_rationals():
+    r = rng(10)
+    M, N = 6, 40
+    acc = r.integers(-2_000_000, 2_000_000, size=(M, N)).astype(np.int32)
+    acc[0, 0] = 0
+    s_x = (r.random(M) * 0.3 + 0.01).astype(np.float32)
+    s_w = np.float32(1.7e-4)
+    bias = bits(r.standard_normal(N) * 0.01)
+    y = oracle.epilogue(acc, s_x, s_w, bias)
+    bias_f = oracle.bf16_bits_to_f32(bias)
+    for m in range(M):
+        alpha = rn_float32(Fraction(float(s_x[m])) * Fraction(float(s_w)))
+        for n in range(N):
+            exact = Fraction(int(acc[m, n])) * alpha + Fraction(float(bias_f[n]))
+            v32 = float(rn_float32(exact))
+            assert y[m, n] == oracle.f32_to_bf16_bits(v32)
+    # no bias: +0
+    y0 = oracle.epilogue(acc, s_x, s_w, None)
+    assert y0[0, 0] == 0x0000
+
+
+def test_epilogue_is_one_fused_rounding():
+    # With bias -1 and acc * alpha within a few float32 ulps of 1, the sum
+    # cancels and rounding the product to float32 first changes the bf16
+    # result.  The oracle must follow the single (fused) rounding.
+    r = rng(13)
+    found = 0
+    for _ in range(20000):
+        alpha = np.float32(r.random() * 1e-4 + 1e-6)
+        a = int(round(1.0 / float(alpha)))
+        exact = Fraction(a) * Fraction(float(alpha)) - 1
+        if exact == 0:
+            continue
+        fused = float(rn_float32(exact))
+        two_step = float(rn_float32(rn_float32(Fraction(a) * Fraction(float(alpha))) - 1))
+        if oracle.f32_to_bf16_bits(fused) != oracle.f32_to_bf16_bits(two_step):
+            y = oracle.epilogue(np.array([[a]], np.int32), np.array([alpha], np.float32),
+                                np.float32(1.0), np.array([0xbf80], np.uint16))   # bias = -1.0
+            assert y[0, 0] == oracle.f32_to_bf16_bits(fused)
+            found += 1
+            if found >= 20:
+                break
+    assert found >= 5
+
+
+# ---------------------------------------------------------------- whole method
+
+def test_linear_rows_equals_full_linear():
+    L = synth.make_layer("tiny")
+    wq, s_w = oracle.quant_weight(L.w, L.g)
+    y, q, s = oracle.linear(L.x_bits, wq, s_w, L.g, L.bias_bits)
+    rows = np.array([0, 5, 77, L.M - 1])
+    y2, q2, s2 = oracle.linear_rows(L.x_bits, rows, wq, s_w, L.g, L.bias_bits)
+    assert np.array_equal(y2, y[rows]) and np.array_equal(q2, q[rows]) and np.array_equal(s2, s[rows])
+
+
+def test_elementwise_error_bound_on_tiny_config():
+    L = synth.make_layer("tiny")
+    wq, s_w, wrot = oracle.quant_weight(L.w, L.g, return_rot=True)
+    q, s, xrot = oracle.quant_act(L.x_bits, L.g, return_rot=True)
+    y = oracle.bf16_bits_to_f32(oracle.epilogue(oracle.gemm_i32(q, wq), s, s_w, L.bias_bits)).astype(np.float64)
+    ref = oracle.reference_fp64(L.x_bits, L.w, L.bias_bits)
+    a, b = np.abs(xrot.astype(np.float64)), np.abs(wrot.astype(np.float64))
+    sx, sw = s.astype(np.float64)[:, None], float(s_w)
+    bound = (a.sum(1)[:, None] * sw / 2 + (b.sum(1)[None, :]) * sx / 2 + L.K * sx * sw / 4
+             + 2.0 ** -8 * np.abs(y) + 1e-5 * (a @ b.T) + 1e-7)
+    assert np.all(np.abs(y - ref) <= bound)
+
+
+def test_nrmse_gate_and_rotation_helps_outliers(golden_dir):
+    gate = read_facts(golden_dir)["nrmse_screening_gate"]
+    L = synth.make_layer("tiny")
+    ref = oracle.reference_fp64(L.x_bits, L.w, L.bias_bits)
+    errs = {}
+    for g in (1, 128, 256):
+        wq, s_w = oracle.quant_weight(L.w, g)
+        y, _, _ = oracle.linear(L.x_bits, wq, s_w, g, L.bias_bits)
+        errs[g] = oracle.nrmse(oracle.bf16_bits_to_f32(y), ref)
+    assert errs[128] <= gate and errs[256] <= gate
+    # "without the rotation a single outlier channel sets the scale for a whole token"
+    assert errs[128] < errs[1] and errs[256] < errs[1]
+
+
+def test_checker_rejects_zero_output_and_flipped_codes(golden_dir):
+    facts = read_facts(golden_dir)
+    L = synth.make_layer("tiny")
+    wq, s_w = oracle.quant_weight(L.w, L.g)
+    y, q, s = oracle.linear(L.x_bits, wq, s_w, L.g, L.bias_bits)
+    yf = oracle.bf16_bits_to_f32(y)
+    assert oracle.nrmse(np.zeros_like(yf), yf) == facts["negative_control_error"]
+    q_bad = q.copy()
+    q_bad[0:16, 0:64] = -q_bad[0:16, 0:64]
+    y_bad = oracle.epilogue(oracle.gemm_i32(q_bad, wq), s, s_w, L.bias_bits)
+    assert oracle.nrmse(oracle.bf16_bits_to_f32(y_bad), yf) > 1e-2
