@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Throughput of the INT8 ConvRot linear layer on one MI355X.
+
+One step = one pass of the layer's hot path over one batch of tokens:
+rotate + per-token int8 quantization of the bf16 activation (one kernel),
+then the int8 x int8 -> int32 MFMA GEMM with the fused dequant + bias bf16
+epilogue (one kernel) -- exactly the two launches convrot_linear makes for a
+batch of at most 2N tokens.  The weight is prepared once beforehand, as the
+pages' checkpoints ship it already rotated and quantized.  Inputs are seeded
+synthetic tensors resident in HBM before the timed region starts.
+
+Workload: the DiT MLP up-projection at 1024^2 -- M = 4608 tokens (4096 image
++ 512 text), K = 3072, N = 12288, group 128, Student-t (df 4) activations with
+outlier channels up to x50.
+
+Printed: one JSON line with the metric (int8 TOPS = 2*M*N*K / step time), the
+roofline of the dominant kernel (the GEMM, timed with HIP events on the stream
+it runs on) and the CPU oracle timed on a bounded sample of token rows.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA: 5.0 POP/s
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E: 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_mlp_up.json")
+GEMM_SOURCES = [os.path.join(ROOT, "w8a8_rotated_int8_convrot_amd", "csrc", "gemm_i8.hip")]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--group", type=int, default=128, choices=(128, 256))
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample (0 disables the cpu_baseline leg)")
+    return p.parse_args()
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs,
+    or None when the GEMM source has changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(L, budget_s):
+    """The CPU oracle (single-threaded C) on a seeded sample of token rows of
+    the same workload, until about budget_s seconds of CPU work."""
+    import numpy as np
+    import oracle
+    from w8a8_rotated_int8_convrot_amd import synth
+
+    wq, s_w = oracle.quant_weight(L.w, L.g)        # offline weight preparation, untimed
+    order = synth.sample_rows(L.M, L.M, 77)        # all rows, seeded order
+    done, t_used, batch = 0, 0.0, 8
+    while t_used < budget_s and done < L.M:
+        rows = order[done:done + batch]
+        t0 = time.perf_counter()
+        oracle.linear_rows(L.x_bits, rows, wq, s_w, L.g, L.bias_bits)
+        t_used += time.perf_counter() - t0
+        done += len(rows)
+        batch = min(64, batch * 2)
+    tops = 2.0 * done * L.N * L.K / t_used / 1e12
+    return {"value": tops, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"{done} seeded token rows of the M={L.M} batch (whole layer per row: "
+                      f"rotate+quantize, int8 GEMM against all N={L.N} channels, epilogue), "
+                      f"{t_used:.1f} s, single-threaded C oracle"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(token- and channel-sharded multi-GPU runs are described in the design notes, "
+              "not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from w8a8_rotated_int8_convrot_amd import binding, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = synth.make_layer("mlp_up", g=args.group)
+    M, K, N, g = L.M, L.K, L.N, L.g
+    x = torch.from_numpy(L.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    w = torch.from_numpy(L.w).to(dev)
+    bias = torch.from_numpy(L.bias_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    wq, s_w = binding.convrot_prepare_weight(w, g)
+    del w
+    q = torch.empty((M, K), dtype=torch.int8, device=dev)
+    s = torch.empty(M, dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(binding.convrot_linear_workspace(M, K, N), dtype=torch.uint8, device=dev)
+    assert binding.convrot_linear_workspace(M, K, N) >= M * K   # one slice: same two launches
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.convrot_rotate_quant(x, g, q, s)
+        binding.convrot_gemm_dequant(q, s, wq, s_w, bias, out=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps; HIP events on the launch stream bracket every GEMM
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        binding.convrot_rotate_quant(x, g, q, s)
+        ev[i][0].record(stream)
+        binding.convrot_gemm_dequant(q, s, wq, s_w, bias, out=y)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # convrot_linear itself (same kernels, one C call), for reference
+    for _ in range(3):
+        binding.convrot_linear(x, wq, s_w, g, bias, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        binding.convrot_linear(x, wq, s_w, g, bias, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    linear_s = (time.perf_counter() - t2) / args.steps
+
+    ops = 2.0 * M * N * K
+    value = ops / step_s / 1e12
+    achieved = ops / (gemm_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+    out = {
+        "metric": "ConvRot linear int8 TOPS + % int8 MFMA peak at M=4608,K=3072,N=12288",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"DiT MLP up-projection at 1024^2 (ConvRot linear): M={M} tokens, "
+                               f"K={K}, N={N}, rotation group {g}, Student-t df4 activations "
+                               f"with outlier channels up to x50, bf16 bias",
+                   "M": M, "K": K, "N": N, "group": g, "parallelism": "single GPU"},
+        "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
+        "convrot_linear_ms": round(linear_s * 1e3, 5),
+        "roofline": {"bound": "mfma", "kernel": "gemm_i8_kernel (GEMM + dequant/bias epilogue)",
+                     "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
+                     "gemm_ms": round(gemm_ms, 5)},
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

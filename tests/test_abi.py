@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+* the library loads and exports every function include/convrot.h declares;
+* argument errors are reported with the documented status before any launch
+  (fake device addresses are passed: a call that got past its checks would
+  touch them, so these tests also show that the checks come first);
+* the workspace contract of the page "int8 Compute", section "Memory": the
+  input is quantized in slices of at most twice the output width, so the
+  working memory stays within the 2*N*K bytes of an unpacked bf16 weight.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convrot.h")
+
+OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE = 0, -1, -2, -3, -4
+A = 0x10000          # a fake, 16-byte aligned device address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def binding():
+    from w8a8_rotated_int8_convrot_amd import binding, build
+    if not os.path.exists(binding.LIB_PATH):
+        build.build()
+    binding.lib()
+    return binding
+
+
+@pytest.fixture(scope="module")
+def lib(binding):
+    return binding.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(convrot_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("convrot_prepare_weight", "convrot_linear", "convrot_rotate_quant",
+              "convrot_gemm_i32", "convrot_gemm_dequant", "convrot_last_error",
+              "convrot_abi_version", "convrot_linear_workspace", "convrot_prepare_weight_workspace"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib, binding):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in binding.SIGNATURES, name
+        assert hasattr(binding, name), name        # Python binding of the same name
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define\s+CONVROT_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert lib.convrot_abi_version() == int(m.group(1))
+
+
+def facts():
+    out = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "pages_facts.txt")):
+        line = line.split("#")[0].split()
+        if line:
+            out[line[0]] = float(line[1])
+    return out
+
+
+@pytest.mark.parametrize("M,K,N", [(4608, 3072, 12288), (4608, 12288, 3072), (16896, 3072, 12288),
+                                   (16, 4096, 12288), (1000, 256, 96), (1, 128, 1)])
+def test_workspace_stays_within_unpacked_weight(lib, M, K, N):
+    per_width = facts()["slice_rows_per_output_width"]
+    S = int(min(M, per_width * N))
+    ws = lib.convrot_linear_workspace(M, K, N)
+    assert ws >= S * K + 4 * S
+    assert ws <= S * K + 4 * S + 256
+    assert ws <= 2 * N * K + 4 * S + 256          # unpacked bf16 weight + the scales
+
+
+def call_linear(lib, x=A, M=64, K=512, wq=A, ws_scale=A, N=64, g=128, bias=None, y=A,
+                ws=A, ws_bytes=1 << 20):
+    return lib.convrot_linear(x, M, K, wq, ws_scale, N, g, bias, y, ws, ws_bytes, None)
+
+
+def test_linear_argument_errors(lib):
+    assert call_linear(lib, g=64) == EUNSUPPORTED
+    assert b"group" in lib.convrot_last_error()
+    assert call_linear(lib, g=512) == EUNSUPPORTED
+    assert call_linear(lib, K=384, g=256) == EINVAL          # K % group != 0
+    assert call_linear(lib, K=131072 + 128) == EINVAL        # K too large for int32 sums
+    assert call_linear(lib, N=0) == EINVAL
+    assert call_linear(lib, M=-1) == EINVAL
+    assert call_linear(lib, x=None) == EINVAL
+    assert call_linear(lib, y=None) == EINVAL
+    assert call_linear(lib, x=A + 8) == EALIGN
+    assert call_linear(lib, y=A + 2) == EALIGN
+    assert call_linear(lib, ws=A + 4) == EALIGN
+    assert call_linear(lib, ws=None) == EWORKSPACE
+    assert call_linear(lib, ws_bytes=15 * (512 + 4)) == EWORKSPACE   # less than one 16-row slice
+    assert b"workspace" in lib.convrot_last_error()
+
+
+def test_empty_batch_needs_nothing(lib):
+    assert call_linear(lib, M=0, x=None, y=None, ws=None, ws_bytes=0) == OK
+    assert lib.convrot_last_error() == b""
+    assert lib.convrot_rotate_quant(None, 0, 256, 128, None, None, None) == OK
+    assert lib.convrot_gemm_dequant(None, None, None, None, None, None, 0, 4, 128, None) == OK
+
+
+def test_stage_argument_errors(lib):
+    assert lib.convrot_rotate_quant(A, 4, 512, 100, A, A, None) == EUNSUPPORTED
+    assert lib.convrot_rotate_quant(A, 4, 640, 256, A, A, None) == EINVAL
+    assert lib.convrot_rotate_quant(A + 1, 4, 512, 128, A, A, None) == EALIGN
+    assert lib.convrot_gemm_i32(A, A, 4, 4, 100, A, None) == EINVAL          # K % 128
+    assert lib.convrot_gemm_i32(A, A, 4, 4, 256, A + 4, None) == EALIGN
+    assert lib.convrot_gemm_i32(A, None, 4, 4, 256, A, None) == EINVAL
+    assert lib.convrot_gemm_dequant(A, A, A, A, None, A + 2, 4, 4, 256, None) == EALIGN
+    assert lib.convrot_gemm_dequant(A, None, A, A, None, A, 4, 4, 256, None) == EINVAL
+
+
+def test_prepare_weight_argument_errors(lib):
+    f = lib.convrot_prepare_weight
+    assert f(A, 7, 64, 512, 128, A, A, A, 256, None) == EUNSUPPORTED       # dtype
+    assert f(A, 0, 64, 512, 64, A, A, A, 256, None) == EUNSUPPORTED        # group
+    assert f(A, 0, 0, 512, 128, A, A, A, 256, None) == EINVAL
+    assert f(A, 0, 64, 500, 128, A, A, A, 256, None) == EINVAL
+    assert f(A, 0, 64, 512, 128, A, A, A, 2, None) == EWORKSPACE
+    assert f(A, 0, 64, 512, 128, A, A, None, 256, None) == EWORKSPACE
+    assert f(A + 4, 0, 64, 512, 128, A, A, A, 256, None) == EALIGN
+    assert lib.convrot_prepare_weight_workspace(64, 512) >= 4
+
+
+def test_binding_refuses_cpu_tensors(binding):
+    import torch
+    with pytest.raises(ValueError):
+        binding.convrot_rotate_quant(torch.zeros((2, 128), dtype=torch.bfloat16), 128)

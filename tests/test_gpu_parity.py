@@ -1,0 +1,243 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: int8 codes, scales and int32 products bit-exact; bf16 outputs within
+relative Frobenius error 1e-2 of the oracle (and bit-exact where the oracle's
+own int8/int32 tensors are fed to the epilogue).  Full-size workloads are run
+whole on the GPU and compared on seeded sampled token rows, which the oracle
+evaluates one by one (each token is quantized on its own, so a sampled row of
+the layer is exactly that row of the full result); weights and scales are
+compared in full.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests._util import bits_of, rel_frobenius, same_bf16, to_dev_bf16
+from w8a8_rotated_int8_convrot_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-2          # bf16 output vs oracle, relative Frobenius
+NRMSE_GATE = 0.05       # quantized output vs unquantized fp64 product
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from w8a8_rotated_int8_convrot_amd import binding
+    binding.lib()
+    return binding
+
+
+DEV = "cuda:0"
+
+
+def rand_bf16(M, K, seed, outliers=4, factor=20.0):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((M, K))
+    if outliers:
+        x[:, r.choice(K, outliers, replace=False)] *= factor
+    return synth.to_bf16_bits(x)
+
+
+# ---------------------------------------------------------------- rotate + quant
+
+ROTQ_CASES = [
+    (5, 128, 128), (131, 512, 128), (300, 3072, 128), (77, 3072, 256), (40, 4096, 128),
+    (33, 12288, 128), (20, 12288, 256), (9, 16384, 128), (7, 24576, 256), (3, 131072, 128),
+]
+
+
+@pytest.mark.parametrize("M,K,g", ROTQ_CASES)
+def test_rotate_quant_bit_exact(B, M, K, g):
+    x = rand_bf16(M, K, seed=M * 7 + K + g)
+    x[0] = 0                                   # a zero token
+    if M > 2:
+        x[1] = 0
+        x[1, K // 3] = synth.to_bf16_bits(np.array([-3.0]))[0]   # a one-hot token
+    q, s = B.convrot_rotate_quant(to_dev_bf16(x, DEV), g)
+    q_ref, s_ref = oracle.quant_act(x, g)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+
+
+# ---------------------------------------------------------------- weights
+
+@pytest.mark.parametrize("N,K,g,dt", [(512, 512, 128, "f32"), (300, 3072, 256, "f32"),
+                                      (1000, 384, 128, "bf16"), (7, 16384, 128, "f32"),
+                                      (33, 12288, 256, "bf16")])
+def test_prepare_weight_bit_exact(B, N, K, g, dt):
+    r = np.random.default_rng(N + K)
+    w = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[N // 2, K // 5] = 0.9                    # one large weight sets the tensor scale
+    if dt == "bf16":
+        wb = synth.to_bf16_bits(w)
+        w = oracle.bf16_bits_to_f32(wb)
+        wt = to_dev_bf16(wb, DEV)
+    else:
+        wt = torch.from_numpy(w).to(DEV)
+    wq, s = B.convrot_prepare_weight(wt, g)
+    wq_ref, s_ref = oracle.quant_weight(w, g)
+    assert np.array_equal(wq.cpu().numpy(), wq_ref)
+    assert s.item() == float(s_ref)
+
+
+def test_prepare_weight_zero(B):
+    wq, s = B.convrot_prepare_weight(torch.zeros((64, 256), device=DEV), 128)
+    assert s.item() == 0.0 and int(wq.abs().max()) == 0
+
+
+# ---------------------------------------------------------------- GEMM stages
+
+GEMM_CASES = [(1, 1, 128), (17, 33, 256), (300, 200, 384), (513, 1000, 1024), (64, 12288, 4096),
+              (2304, 2560, 640), (4608, 12288, 3072)]
+
+
+def rand_i8(shape, seed):
+    return np.random.default_rng(seed).integers(-127, 128, size=shape, dtype=np.int64).astype(np.int8)
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_CASES)
+def test_gemm_i32_bit_exact(B, M, N, K):
+    a = rand_i8((M, K), M + 3 * N + K)
+    b = rand_i8((N, K), M * N + K)
+    acc = B.convrot_gemm_i32(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV))
+    rows = synth.sample_rows(M, 48, M + N) if M * N * K > 2e9 else np.arange(M)
+    got = acc[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    assert np.array_equal(got, oracle.gemm_i32(a[rows], b))
+
+
+def test_gemm_i32_extreme_accumulators(B):
+    K = 131072
+    a = np.full((3, K), 127, np.int8)
+    a[1] = -127
+    b = np.full((5, K), 127, np.int8)
+    b[2] = -127
+    b[4, ::2] = -127
+    acc = B.convrot_gemm_i32(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)).cpu().numpy()
+    assert np.array_equal(acc, oracle.gemm_i32(a, b))
+    assert acc[0, 0] == 127 * 127 * K
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 33, 256), (300, 1001, 384), (513, 1000, 1024), (4608, 12288, 3072)])
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_gemm_dequant_bit_exact(B, M, N, K, with_bias):
+    r = np.random.default_rng(M + N)
+    a = rand_i8((M, K), M + N + K)
+    b = rand_i8((N, K), 3 * M + N)
+    s_x = (r.random(M) * 0.2 + 1e-3).astype(np.float32)
+    s_w = np.float32(2.3e-4)
+    bias = synth.to_bf16_bits(r.standard_normal(N) * 0.01) if with_bias else None
+    y = B.convrot_gemm_dequant(torch.from_numpy(a).to(DEV), torch.from_numpy(s_x).to(DEV),
+                               torch.from_numpy(b).to(DEV), torch.tensor([s_w], device=DEV),
+                               None if bias is None else to_dev_bf16(bias, DEV))
+    rows = synth.sample_rows(M, 48, M) if M * N * K > 2e9 else np.arange(M)
+    got = bits_of(y[torch.from_numpy(rows).to(DEV)])
+    ref = oracle.epilogue(oracle.gemm_i32(a[rows], b), s_x[rows], s_w, bias)
+    assert np.all(same_bf16(got, ref))
+
+
+# ---------------------------------------------------------------- whole layer
+
+E2E = [("tiny", 128), ("tiny", 256), ("qkv", 128), ("mlp_up", 128), ("mlp_up", 256),
+       ("mlp_down", 128), ("hires_up", 128), ("small_m", 128),
+       ("stack_b0_qkv", 128), ("stack_b0_out", 128), ("stack_b59_up", 128), ("stack_b59_down", 128)]
+
+
+def run_layer(B, L):
+    x = to_dev_bf16(L.x_bits, DEV)
+    w = torch.from_numpy(L.w).to(DEV)
+    bias = to_dev_bf16(L.bias_bits, DEV)
+    wq, s_w = B.convrot_prepare_weight(w, L.g)
+    y = B.convrot_linear(x, wq, s_w, L.g, bias)
+    q, s = B.convrot_rotate_quant(x, L.g)
+    return x, wq, s_w, bias, y, q, s
+
+
+@pytest.mark.parametrize("name,g", E2E)
+def test_linear_end_to_end(B, name, g):
+    L = synth.make_layer(name, g=g)
+    x, wq, s_w, bias, y, q, s = run_layer(B, L)
+    torch.cuda.synchronize()
+
+    wq_ref, s_w_ref = oracle.quant_weight(L.w, L.g)
+    assert np.array_equal(wq.cpu().numpy(), wq_ref), "weight codes"
+    assert s_w.item() == float(s_w_ref), "weight scale"
+
+    rows = np.arange(L.M) if L.M <= 256 else synth.sample_rows(L.M, 64, L.M + L.N)
+    y_ref, q_ref, s_ref = oracle.linear_rows(L.x_bits, rows, wq_ref, s_w_ref, L.g, L.bias_bits)
+    ridx = torch.from_numpy(rows).to(DEV)
+    q_gpu = q[ridx].cpu().numpy()
+    # activation codes: bit-exact (and therefore 100 % identical, none off by > 1)
+    assert np.array_equal(q_gpu, q_ref), f"codes differ at {np.argwhere(q_gpu != q_ref)[:5]}"
+    assert np.array_equal(s[ridx].cpu().numpy(), s_ref), "token scales"
+
+    y_gpu = bits_of(y[ridx])
+    assert np.all(np.isfinite(oracle.bf16_bits_to_f32(y_gpu)))
+    err = rel_frobenius(y_gpu, y_ref)
+    assert err <= REL_TOL, f"rel-Frobenius {err}"
+    # with identical codes the epilogue is deterministic: expect every value equal
+    assert np.mean(same_bf16(y_gpu, y_ref)) == 1.0
+
+    # sanity gate against the unquantized product
+    ref64 = oracle.reference_fp64(L.x_bits[rows], L.w, L.bias_bits)
+    assert oracle.nrmse(oracle.bf16_bits_to_f32(y_gpu), ref64) <= NRMSE_GATE
+
+
+# ---------------------------------------------------------------- invariances and edges
+
+def test_result_does_not_depend_on_slicing(B):
+    L = synth.make_layer("tiny")
+    x, wq, s_w, bias, y, _, _ = run_layer(B, L)
+    full = bits_of(y)
+    for rows in (16, 48, 112):
+        ws = torch.empty(rows * L.K + 256 + rows * 4, dtype=torch.uint8, device=DEV)
+        y2 = B.convrot_linear(x, wq, s_w, L.g, bias, workspace=ws)
+        assert np.array_equal(bits_of(y2), full), rows
+
+
+def test_slicing_at_twice_the_output_width(B):
+    # M > 2N: the default workspace holds 2N tokens, so the call runs in slices
+    r = np.random.default_rng(4)
+    M, K, N = 1000, 256, 96
+    xb = rand_bf16(M, K, 5)
+    w = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    x = to_dev_bf16(xb, DEV)
+    wq, s_w = B.convrot_prepare_weight(torch.from_numpy(w).to(DEV), 128)
+    assert B.convrot_linear_workspace(M, K, N) < M * K
+    y = B.convrot_linear(x, wq, s_w, 128)
+    wq_ref, s_ref = oracle.quant_weight(w, 128)
+    y_ref, _, _ = oracle.linear(xb, wq_ref, s_ref, 128)
+    assert np.all(same_bf16(bits_of(y), y_ref))
+
+
+def test_bit_identical_run_to_run(B):
+    L = synth.make_layer("qkv", M=1024)
+    x, wq, s_w, bias, y, q, s = run_layer(B, L)
+    y2 = B.convrot_linear(x, wq, s_w, L.g, bias)
+    q2, s2 = B.convrot_rotate_quant(x, L.g)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(q, q2) and torch.equal(s, s2)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (1, 3, 256), (2, 5, 128), (16, 12288, 4096), (63, 130, 512)])
+def test_small_and_ragged_shapes(B, M, N, K):
+    r = np.random.default_rng(M + N + K)
+    xb = rand_bf16(M, K, M + K, outliers=0)
+    w = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bias = synth.to_bf16_bits(r.standard_normal(N) * 0.01)
+    wq, s_w = B.convrot_prepare_weight(torch.from_numpy(w).to(DEV), 128)
+    y = B.convrot_linear(to_dev_bf16(xb, DEV), wq, s_w, 128, to_dev_bf16(bias, DEV))
+    wq_ref, s_ref = oracle.quant_weight(w, 128)
+    y_ref, _, _ = oracle.linear(xb, wq_ref, s_ref, 128, bias)
+    assert np.all(same_bf16(bits_of(y), y_ref))
+
+
+def test_empty_batch_is_a_no_op(B):
+    wq = torch.zeros((8, 128), dtype=torch.int8, device=DEV)
+    s_w = torch.ones(1, device=DEV)
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
+    y = B.convrot_linear(x, wq, s_w, 128)
+    assert y.shape == (0, 8)

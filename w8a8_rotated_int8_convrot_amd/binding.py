@@ -1,0 +1,200 @@
+"""Python binding of ``libconvrot.so`` (C ABI: ``include/convrot.h``).
+
+Argument marshalling only: every function here allocates its torch outputs
+(device memory is PyTorch's job), passes raw device pointers and the current
+HIP stream to the entry point of the same name, and raises on a non-zero
+status.  Every step of the layer runs in the library's HIP kernels; there is
+no other implementation to fall back to, and importing this module without a
+built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconvrot.so")
+
+CONVROT_F32 = 0
+CONVROT_BF16 = 1
+
+STATUS = {0: "CONVROT_OK", -1: "CONVROT_EINVAL", -2: "CONVROT_EUNSUPPORTED",
+          -3: "CONVROT_EALIGN", -4: "CONVROT_EWORKSPACE", -5: "CONVROT_EHIP"}
+
+# Every symbol include/convrot.h declares, with (argtypes, restype).
+_P, _I64, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "convrot_abi_version": ([], _I),
+    "convrot_last_error": ([], ctypes.c_char_p),
+    "convrot_prepare_weight_workspace": ([_I64, _I64], _SZ),
+    "convrot_prepare_weight": ([_P, _I, _I64, _I64, _I, _P, _P, _P, _SZ, _P], _I),
+    "convrot_linear_workspace": ([_I64, _I64, _I64], _SZ),
+    "convrot_linear": ([_P, _I64, _I64, _P, _P, _I64, _I, _P, _P, _P, _SZ, _P], _I),
+    "convrot_rotate_quant": ([_P, _I64, _I64, _I, _P, _P, _P], _I),
+    "convrot_gemm_i32": ([_P, _P, _I64, _I64, _I64, _P, _P], _I),
+    "convrot_gemm_dequant": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _I),
+}
+
+
+class ConvrotError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} -> {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loads it on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m w8a8_rotated_int8_convrot_amd.build` first")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = l
+    return _lib
+
+
+def _call(name, *args):
+    rc = getattr(lib(), name)(*args)
+    if rc != 0:
+        raise ConvrotError(name, rc, last_error())
+    return rc
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t, dtype, name, ndim=None):
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous {dtype} CUDA tensor, got "
+                         f"{t.dtype} on {t.device} (contiguous={t.is_contiguous()})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dimensions, got {t.dim()}")
+
+
+def convrot_last_error() -> str:
+    return lib().convrot_last_error().decode()
+
+
+last_error = convrot_last_error
+
+
+def convrot_abi_version() -> int:
+    return lib().convrot_abi_version()
+
+
+def convrot_prepare_weight_workspace(N: int, K: int) -> int:
+    return lib().convrot_prepare_weight_workspace(N, K)
+
+
+def convrot_linear_workspace(M: int, K: int, N: int) -> int:
+    return lib().convrot_linear_workspace(M, K, N)
+
+
+def convrot_prepare_weight(w: torch.Tensor, group: int):
+    """fp32 or bf16 weight [N, K] -> (int8 codes [N, K], fp32 scale [1])."""
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("convrot_prepare_weight: weight must be float32 or bfloat16")
+    _need(w, w.dtype, "w", 2)
+    N, K = w.shape
+    wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
+    s = torch.empty(1, dtype=torch.float32, device=w.device)
+    ws_bytes = convrot_prepare_weight_workspace(N, K)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=w.device)
+    dt = CONVROT_F32 if w.dtype == torch.float32 else CONVROT_BF16
+    _call("convrot_prepare_weight", _ptr(w), dt, N, K, group, _ptr(wq), _ptr(s), _ptr(ws),
+          ws_bytes, _stream(w))
+    return wq, s
+
+
+def convrot_rotate_quant(x: torch.Tensor, group: int, q=None, s=None):
+    """bf16 [M, K] -> (int8 codes [M, K], fp32 scales [M])."""
+    _need(x, torch.bfloat16, "x", 2)
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=x.device) if q is None else q
+    s = torch.empty(M, dtype=torch.float32, device=x.device) if s is None else s
+    _need(q, torch.int8, "q", 2)
+    _need(s, torch.float32, "s", 1)
+    if tuple(q.shape) != (M, K) or s.numel() != M:
+        raise ValueError("convrot_rotate_quant: output shape mismatch")
+    _call("convrot_rotate_quant", _ptr(x), M, K, group, _ptr(q), _ptr(s), _stream(x))
+    return q, s
+
+
+def convrot_gemm_i32(xq: torch.Tensor, wq: torch.Tensor) -> torch.Tensor:
+    """int8 [M, K] x int8 [N, K]^T -> int32 [M, N]."""
+    _need(xq, torch.int8, "xq", 2)
+    _need(wq, torch.int8, "wq", 2)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("convrot_gemm_i32: K mismatch")
+    acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    _call("convrot_gemm_i32", _ptr(xq), _ptr(wq), M, N, K, _ptr(acc), _stream(xq))
+    return acc
+
+
+def convrot_gemm_dequant(xq, x_scale, wq, w_scale, bias=None, out=None) -> torch.Tensor:
+    """int8 codes and scales -> bf16 [M, N] (GEMM + dequant + bias)."""
+    _need(xq, torch.int8, "xq", 2)
+    _need(wq, torch.int8, "wq", 2)
+    _need(x_scale, torch.float32, "x_scale", 1)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or x_scale.numel() != M:
+        raise ValueError("convrot_gemm_dequant: shape mismatch")
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias", 1)
+        if bias.numel() != N:
+            raise ValueError("convrot_gemm_dequant: bias must have N elements")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device) if out is None else out
+    _need(y, torch.bfloat16, "out", 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("convrot_gemm_dequant: output shape mismatch")
+    _call("convrot_gemm_dequant", _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias),
+          _ptr(y), M, N, K, _stream(xq))
+    return y
+
+
+def convrot_linear(x, wq, w_scale, group, bias=None, out=None, workspace=None) -> torch.Tensor:
+    """The whole layer: bf16 x [M, K], int8 wq [N, K] (+ scale) -> bf16 y [M, N].
+
+    ``workspace`` (uint8 CUDA tensor) defaults to convrot_linear_workspace
+    bytes; a smaller one makes the library process the tokens in more
+    slices (same result)."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(wq, torch.int8, "wq", 2)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("convrot_linear: K mismatch")
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias", 1)
+        if bias.numel() != N:
+            raise ValueError("convrot_linear: bias must have N elements")
+    if workspace is None:
+        workspace = torch.empty(max(convrot_linear_workspace(M, K, N), 1), dtype=torch.uint8,
+                                device=x.device)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need(y, torch.bfloat16, "out", 2)
+    _need(workspace, torch.uint8, "workspace")
+    if tuple(y.shape) != (M, N):
+        raise ValueError("convrot_linear: output shape mismatch")
+    _call("convrot_linear", _ptr(x), M, K, _ptr(wq), _ptr(w_scale), N, group, _ptr(bias), _ptr(y),
+          _ptr(workspace), workspace.numel(), _stream(x))
+    return y

@@ -1,0 +1,187 @@
+// convrot_api.hip -- the C ABI declared in include/convrot.h: argument checks,
+// workspace carving, M-slicing and kernel dispatch.  No entry point allocates
+// device memory, synchronises the device or falls back to another path.
+#include "../../include/convrot.h"
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "convrot_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return CONVROT_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CONVROT_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Checks shared by the entry points that take a K dimension of codes.
+int check_k(int64_t K, const char* who) {
+  if (K < 128 || K > convrot::kMaxK || K % 128 != 0)
+    return fail(CONVROT_EINVAL, "%s: K=%lld must be a multiple of 128 in [128, %lld]", who,
+                static_cast<long long>(K), static_cast<long long>(convrot::kMaxK));
+  return CONVROT_OK;
+}
+
+int check_group(int group, int64_t K, const char* who) {
+  if (group != 128 && group != 256)
+    return fail(CONVROT_EUNSUPPORTED, "%s: group %d is not supported (128 or 256)", who, group);
+  if (K < group || K % group != 0 || K > convrot::kMaxK)
+    return fail(CONVROT_EINVAL, "%s: K=%lld must be a positive multiple of the group %d, at most %lld",
+                who, static_cast<long long>(K), group, static_cast<long long>(convrot::kMaxK));
+  return CONVROT_OK;
+}
+
+// Rows and columns are passed to kernels as int; keep every product in range.
+int check_mn(int64_t M, int64_t N, const char* who) {
+  if (M < 0 || N < 1 || M > (int64_t(1) << 30) || N > (int64_t(1) << 30))
+    return fail(CONVROT_EINVAL, "%s: M=%lld N=%lld out of range (0 <= M, 1 <= N, both <= 2^30)", who,
+                static_cast<long long>(M), static_cast<long long>(N));
+  return CONVROT_OK;
+}
+
+// Slice height of convrot_linear for a given workspace.
+int64_t slice_rows(int64_t M, int64_t K, int64_t N, size_t ws_bytes) {
+  const int64_t cap = M < 2 * N ? M : 2 * N;
+  // codes [S, K] rounded to 256 bytes, then S floats
+  int64_t fit = static_cast<int64_t>(ws_bytes / static_cast<size_t>(K + 4));
+  while (fit > 0 && round_up(static_cast<size_t>(fit) * K, 256) + static_cast<size_t>(fit) * 4 > ws_bytes) --fit;
+  if (fit >= cap) return cap;
+  fit -= fit % 16;
+  return fit;
+}
+
+}  // namespace
+
+extern "C" {
+
+int convrot_abi_version(void) { return CONVROT_ABI_VERSION; }
+
+const char* convrot_last_error(void) { return g_last_error; }
+
+size_t convrot_prepare_weight_workspace(int64_t, int64_t) { return 256; }
+
+int convrot_prepare_weight(const void* w, int w_dtype, int64_t N, int64_t K, int group,
+                           int8_t* wq_out, float* w_scale_out, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  const char* who = "convrot_prepare_weight";
+  if (int rc = check_group(group, K, who)) return rc;
+  if (N < 1 || N > (int64_t(1) << 31) - 1)
+    return fail(CONVROT_EINVAL, "%s: N=%lld must be in [1, 2^31)", who, static_cast<long long>(N));
+  if (w_dtype != CONVROT_F32 && w_dtype != CONVROT_BF16)
+    return fail(CONVROT_EUNSUPPORTED, "%s: weight dtype %d (CONVROT_F32 or CONVROT_BF16)", who, w_dtype);
+  if (!w || !wq_out || !w_scale_out) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
+  if (!aligned16(w) || !aligned16(wq_out) || (workspace && !aligned16(workspace)))
+    return fail(CONVROT_EALIGN, "%s: w, wq_out and workspace must be 16-byte aligned", who);
+  if (!workspace || ws_bytes < convrot_prepare_weight_workspace(N, K))
+    return fail(CONVROT_EWORKSPACE, "%s: workspace of %zu bytes needed", who,
+                convrot_prepare_weight_workspace(N, K));
+  hipError_t e = convrot::launch_prepare_weight(w, w_dtype == CONVROT_BF16, N, K, group, wq_out,
+                                                w_scale_out, static_cast<uint32_t*>(workspace),
+                                                static_cast<hipStream_t>(stream));
+  return hip_status(e, who);
+}
+
+size_t convrot_linear_workspace(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || K < 1 || N < 1) return 0;
+  const int64_t S = M < 2 * N ? M : 2 * N;
+  return round_up(static_cast<size_t>(S) * static_cast<size_t>(K), 256) + static_cast<size_t>(S) * 4;
+}
+
+int convrot_rotate_quant(const void* x_bf16, int64_t M, int64_t K, int group, int8_t* xq,
+                         float* x_scale, void* stream) {
+  const char* who = "convrot_rotate_quant";
+  if (int rc = check_group(group, K, who)) return rc;
+  if (M < 0 || M > (int64_t(1) << 31) - 1)
+    return fail(CONVROT_EINVAL, "%s: M=%lld must be in [0, 2^31)", who, static_cast<long long>(M));
+  if (M == 0) return ok();
+  if (!x_bf16 || !xq || !x_scale) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
+  if (!aligned16(x_bf16) || !aligned16(xq))
+    return fail(CONVROT_EALIGN, "%s: x and xq must be 16-byte aligned", who);
+  hipError_t e = convrot::launch_rotate_quant(static_cast<const uint16_t*>(x_bf16), M, K, group, xq,
+                                              x_scale, static_cast<hipStream_t>(stream));
+  return hip_status(e, who);
+}
+
+int convrot_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64_t K,
+                     int32_t* acc, void* stream) {
+  const char* who = "convrot_gemm_i32";
+  if (int rc = check_k(K, who)) return rc;
+  if (int rc = check_mn(M, N, who)) return rc;
+  if (M == 0) return ok();
+  if (!xq || !wq || !acc) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
+  if (!aligned16(xq) || !aligned16(wq) || !aligned16(acc))
+    return fail(CONVROT_EALIGN, "%s: xq, wq and acc must be 16-byte aligned", who);
+  hipError_t e = convrot::launch_gemm_i32(xq, wq, acc, M, N, K, static_cast<hipStream_t>(stream));
+  return hip_status(e, who);
+}
+
+int convrot_gemm_dequant(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                         const float* w_scale, const void* bias_bf16, void* y_bf16, int64_t M,
+                         int64_t N, int64_t K, void* stream) {
+  const char* who = "convrot_gemm_dequant";
+  if (int rc = check_k(K, who)) return rc;
+  if (int rc = check_mn(M, N, who)) return rc;
+  if (M == 0) return ok();
+  if (!xq || !x_scale || !wq || !w_scale || !y_bf16) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
+  if (!aligned16(xq) || !aligned16(wq) || !aligned16(y_bf16))
+    return fail(CONVROT_EALIGN, "%s: xq, wq and y must be 16-byte aligned", who);
+  hipError_t e = convrot::launch_gemm_dequant(xq, x_scale, wq, w_scale,
+                                              static_cast<const uint16_t*>(bias_bf16),
+                                              static_cast<uint16_t*>(y_bf16), M, N, K,
+                                              static_cast<hipStream_t>(stream));
+  return hip_status(e, who);
+}
+
+int convrot_linear(const void* x_bf16, int64_t M, int64_t K, const int8_t* wq, const float* w_scale,
+                   int64_t N, int group, const void* bias_bf16, void* y_bf16, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  const char* who = "convrot_linear";
+  if (int rc = check_group(group, K, who)) return rc;
+  if (int rc = check_mn(M, N, who)) return rc;
+  if (M == 0) return ok();
+  if (!x_bf16 || !wq || !w_scale || !y_bf16) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
+  if (!aligned16(x_bf16) || !aligned16(wq) || !aligned16(y_bf16) || (workspace && !aligned16(workspace)))
+    return fail(CONVROT_EALIGN, "%s: x, wq, y and workspace must be 16-byte aligned", who);
+  const int64_t S = workspace ? slice_rows(M, K, N, ws_bytes) : 0;
+  const int64_t need = M < 16 ? M : 16;
+  if (S < need)
+    return fail(CONVROT_EWORKSPACE, "%s: workspace of %zu bytes holds %lld rows; at least %lld needed "
+                "(convrot_linear_workspace gives %zu)", who, ws_bytes, static_cast<long long>(S),
+                static_cast<long long>(need), convrot_linear_workspace(M, K, N));
+  auto* xq = static_cast<int8_t*>(workspace);
+  auto* xs = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(static_cast<size_t>(S) * K, 256));
+  const auto* x = static_cast<const uint16_t*>(x_bf16);
+  auto* y = static_cast<uint16_t*>(y_bf16);
+  const auto* bias = static_cast<const uint16_t*>(bias_bf16);
+  auto s = static_cast<hipStream_t>(stream);
+  for (int64_t r0 = 0; r0 < M; r0 += S) {
+    const int64_t rows = (M - r0) < S ? (M - r0) : S;
+    hipError_t e = convrot::launch_rotate_quant(x + r0 * K, rows, K, group, xq, xs, s);
+    if (e != hipSuccess) return hip_status(e, who);
+    e = convrot::launch_gemm_dequant(xq, xs, wq, w_scale, bias, y + r0 * N, rows, N, K, s);
+    if (e != hipSuccess) return hip_status(e, who);
+  }
+  return ok();
+}
+
+}  // extern "C"

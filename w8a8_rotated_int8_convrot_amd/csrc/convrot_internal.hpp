@@ -1,0 +1,42 @@
+// convrot_internal.hpp -- shared declarations of the HIP library (not part of
+// the C ABI).  Kernels live in rotate_quant.hip and gemm_i8.hip; argument
+// checking and dispatch live in convrot_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace convrot {
+
+// Largest K the library accepts: 127 * 127 * K must stay below 2^31 so that
+// an int32 accumulator cannot overflow.
+constexpr int64_t kMaxK = 131072;
+
+// ---------------------------------------------------------------- rotate + quant
+
+// Per-token rotate + quantize of a bf16 [M, K] activation into int8 codes and
+// fp32 scales.  group is 128 or 256; K % group == 0.
+hipError_t launch_rotate_quant(const uint16_t* x, int64_t M, int64_t K, int group,
+                               int8_t* q, float* scale, hipStream_t stream);
+
+// Tensorwise weight preparation.  `in_bf16` selects the input type (fp32
+// otherwise).  `amax_cell` is one 4-byte device word of scratch.
+hipError_t launch_prepare_weight(const void* w, bool in_bf16, int64_t N, int64_t K, int group,
+                                 int8_t* wq, float* w_scale, uint32_t* amax_cell,
+                                 hipStream_t stream);
+
+// ---------------------------------------------------------------- GEMM
+
+// GEMM + fused dequant/bias epilogue: y[m][n] (bf16) from xq [M, K] and
+// wq [N, K].  K % 128 == 0.
+hipError_t launch_gemm_dequant(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                               const float* w_scale, const uint16_t* bias, uint16_t* y,
+                               int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// Same main loop with the raw int32 products stored.
+hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
+                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+}  // namespace convrot

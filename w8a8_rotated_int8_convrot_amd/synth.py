@@ -39,28 +39,49 @@ def stream_seed(config: int, layer: int, tensor_id: int) -> int:
     return SEED_BASE + 1000 * config + 10 * layer + tensor_id
 
 
+_CHUNK = 1 << 20
+
+
 def splitmix64(seed: int, n: int, offset: int = 0) -> np.ndarray:
     """Outputs offset .. offset+n-1 of the counter-based SplitMix64 stream."""
+    out = np.empty(n, dtype=np.uint64)
+    s = np.uint64(seed & 0xFFFFFFFFFFFFFFFF)
     with np.errstate(over="ignore"):
-        i = np.arange(offset + 1, offset + n + 1, dtype=np.uint64)
-        z = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) + i * _GOLDEN
-        z = (z ^ (z >> np.uint64(30))) * _M1
-        z = (z ^ (z >> np.uint64(27))) * _M2
-        z = z ^ (z >> np.uint64(31))
-    return z
+        for a in range(0, n, _CHUNK):
+            b = min(n, a + _CHUNK)
+            z = out[a:b]
+            z[:] = np.arange(offset + a + 1, offset + b + 1, dtype=np.uint64)
+            z *= _GOLDEN
+            z += s
+            z ^= z >> np.uint64(30)
+            z *= _M1
+            z ^= z >> np.uint64(27)
+            z *= _M2
+            z ^= z >> np.uint64(31)
+    return out
 
 
 def uniform(seed: int, n: int, offset: int = 0) -> np.ndarray:
     """float64 uniforms in [0, 1)."""
-    return (splitmix64(seed, n, offset) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+    z = splitmix64(seed, n, offset)
+    z >>= np.uint64(11)
+    u = z.astype(np.float64)
+    u *= 2.0 ** -53
+    return u
 
 
 def normal(seed: int, n: int) -> np.ndarray:
     """float64 standard normals (Box-Muller, cosine branch; 2 uniforms each)."""
-    u = uniform(seed, 2 * n)
-    u1 = 1.0 - u[0::2]          # (0, 1]
-    u2 = u[1::2]
-    return np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)
+    u = uniform(seed, 2 * n).reshape(n, 2)
+    out = np.empty(n, dtype=np.float64)
+    for a in range(0, n, _CHUNK):
+        b = min(n, a + _CHUNK)
+        r = np.log(1.0 - u[a:b, 0])      # 1 - u in (0, 1]
+        r *= -2.0
+        np.sqrt(r, out=r)
+        c = np.cos(2.0 * np.pi * u[a:b, 1])
+        np.multiply(r, c, out=out[a:b])
+    return out
 
 
 def student_t4(seed: int, n: int) -> np.ndarray:
