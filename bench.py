@@ -41,7 +41,20 @@ def parse():
     p.add_argument("--group", type=int, default=128, choices=(128, 256))
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample (0 disables the cpu_baseline leg)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="only run 5 plain device-to-device copies of BYTES bytes (the known-size "
+                        "kernel that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
     return p.parse_args()
+
+
+def copy_calibration(nbytes):
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
 def gemm_source_hash():
@@ -96,6 +109,9 @@ def main():
               "(token- and channel-sharded multi-GPU runs are described in the design notes, "
               "not built)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch
