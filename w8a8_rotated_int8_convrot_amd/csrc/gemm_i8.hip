@@ -167,14 +167,13 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
 
   for (int kt = 0; kt < KT; ++kt) {
     const int stage = (kt & 1) * (T::kStageBytes / 16);
-    const bool more = kt + 1 < KT;
-    if (more) {
-      const int64_t k0 = static_cast<int64_t>(kt + 1) * T::BK;
+    // fetch slab kt+1 (the last iteration re-fetches its own slab into the
+    // stage nobody reads any more, which keeps the loop free of branches)
+    const int64_t k0 = static_cast<int64_t>(kt + 1 < KT ? kt + 1 : kt) * T::BK;
 #pragma unroll
-      for (int i = 0; i < T::kALoads; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
+    for (int i = 0; i < T::kALoads; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
 #pragma unroll
-      for (int i = 0; i < T::kBLoads; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + k0);
-    }
+    for (int i = 0; i < T::kBLoads; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + k0);
 #pragma unroll
     for (int kk = 0; kk < T::BK / 64; ++kk) {
       v4i af[T::TN], bf[T::TM];
@@ -194,13 +193,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
         for (int j = 0; j < T::TM; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      const int next = ((kt + 1) & 1) * (T::kStageBytes / 16);
+    const int next = (T::kStageBytes / 16) - stage;
 #pragma unroll
-      for (int i = 0; i < T::kALoads; ++i) lds[next + a_dst[i]] = ra[i];
+    for (int i = 0; i < T::kALoads; ++i) lds[next + a_dst[i]] = ra[i];
 #pragma unroll
-      for (int i = 0; i < T::kBLoads; ++i) lds[next + b_dst[i]] = rb[i];
-    }
+    for (int i = 0; i < T::kBLoads; ++i) lds[next + b_dst[i]] = rb[i];
     __syncthreads();
   }
 
