@@ -241,3 +241,23 @@ def test_empty_batch_is_a_no_op(B):
     x = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
     y = B.convrot_linear(x, wq, s_w, 128)
     assert y.shape == (0, 8)
+
+
+@pytest.mark.parametrize("tile", ["big", "big8", "wide", "mid"])
+@pytest.mark.parametrize("M,N,K", [(300, 1001, 384), (513, 1000, 1024), (1111, 777, 640)])
+def test_every_gemm_tile_is_bit_exact(B, tile, M, N, K, monkeypatch):
+    # the tile shape is a performance choice: every one must give the same bytes
+    monkeypatch.setenv("CONVROT_GEMM_TILE", tile)
+    r = np.random.default_rng(M + N + K)
+    a = rand_i8((M, K), 5 * M + K)
+    b = rand_i8((N, K), 7 * N + K)
+    s_x = (r.random(M) * 0.2 + 1e-3).astype(np.float32)
+    s_w = np.float32(1.1e-4)
+    bias = synth.to_bf16_bits(r.standard_normal(N) * 0.01)
+    ad, bd = torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)
+    acc = B.convrot_gemm_i32(ad, bd).cpu().numpy()
+    y = B.convrot_gemm_dequant(ad, torch.from_numpy(s_x).to(DEV), bd, torch.tensor([s_w], device=DEV),
+                               to_dev_bf16(bias, DEV))
+    acc_ref = oracle.gemm_i32(a, b)
+    assert np.array_equal(acc, acc_ref)
+    assert np.all(same_bf16(bits_of(y), oracle.epilogue(acc_ref, s_x, s_w, bias)))

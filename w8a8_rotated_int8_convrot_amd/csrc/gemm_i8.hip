@@ -19,14 +19,15 @@
 //  * Global -> LDS by direct-to-LDS loads (global_load_lds_dwordx4: each
 //    wave instruction fills 1 KB = 16 LDS rows of 64 bytes, no registers
 //    involved), four LDS stages of one 64-byte k slab each, prefetched three
-//    slabs ahead.  A slab is consumed after `s_waitcnt vmcnt` (this wave's
+//    slabs ahead.  A slab's fragments are read into registers one step before
+//    its MFMAs run (two register sets), after `s_waitcnt vmcnt` (this wave's
 //    loads of that slab have landed) and one `s_barrier` (so have everyone
 //    else's, and everyone is done with the stage about to be refilled).
-//  * LDS rows are 64 bytes; the four 16-byte chunks of row r are stored XOR
-//    (r >> 1) & 3, so the 8 rows served together by one ds_read_b128 pass
-//    fall into distinct banks.  A lane's direct-to-LDS slot is fixed by its
-//    lane id, so the swizzle is applied by choosing which global chunk the
-//    lane fetches.
+//  * LDS rows are 64 bytes; the four 16-byte chunks of a row are stored
+//    XOR-swizzled by row bits (swz below), so the lanes served together by
+//    one ds_read_b128 pass fall into distinct banks.  A lane's direct-to-LDS
+//    slot is fixed by its lane id, so the swizzle is applied by choosing
+//    which global chunk the lane fetches.
 //  * Epilogue: dequant + bias in registers, bf16 tile staged through LDS
 //    (chunk-XOR-swizzled rows), then written out as full contiguous rows with
 //    16-byte stores, so every output line leaves the CU whole.
@@ -36,6 +37,9 @@
 //    tiles of one XCD share weight and activation rows in its L2.
 //  * Ragged edges: rows past M or N are loaded from the last valid row (the
 //    results are discarded) and stores are masked; K is a multiple of 128.
+#include <cstdlib>
+#include <cstring>
+
 #include "convrot_internal.hpp"
 
 namespace convrot {
@@ -48,33 +52,74 @@ typedef const __attribute__((address_space(1))) void glb_void_t;
 constexpr int kBK = 64;        // bytes of K per LDS stage (one MFMA k step)
 constexpr int kStages = 4;     // LDS stages; slabs are prefetched kStages-1 ahead
 
-template <int BN_, int BM_, int WN_, int WM_, int GROUP_M_>
+template <int BN_, int BM_, int WN_, int WM_, int MF_, int GROUP_M_>
 struct Tile {
   static constexpr int BN = BN_;          // output channels per workgroup
   static constexpr int BM = BM_;          // tokens per workgroup
   static constexpr int WN = WN_;          // waves along n
   static constexpr int WM = WM_;          // waves along m
+  static constexpr int MF = MF_;          // MFMA block: 16 (16x16x64) or 32 (32x32x32)
   static constexpr int kGroupM = GROUP_M_;
   static constexpr int kWaves = WN * WM;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kWaveN = BN / WN, kWaveM = BM / WM;
-  static constexpr int TN = kWaveN / 16, TM = kWaveM / 16;
+  static constexpr int TN = kWaveN / MF, TM = kWaveM / MF;   // MFMA blocks per wave
+  static constexpr int kKSteps = MF == 16 ? 1 : 2;           // MFMA k steps per 64-byte slab
+  static constexpr int kAccRegs = MF == 16 ? 4 : 16;
   static constexpr int kStageBytes = (BN + BM) * kBK;
   static constexpr int kLdsBytes = kStages * kStageBytes;
   // direct-to-LDS instructions per wave and slab (each moves 16 rows)
   static constexpr int kALoads = BN / 16 / kWaves;
   static constexpr int kBLoads = BM / 16 / kWaves;
   static constexpr int kLoads = kALoads + kBLoads;
-  static_assert(BN % (WN * 16) == 0 && BM % (WM * 16) == 0, "wave tile");
+  static_assert(MF == 16 || MF == 32, "MFMA shape");
+  static_assert(BN % (WN * MF) == 0 && BM % (WM * MF) == 0, "wave tile");
   static_assert(kALoads * kWaves * 16 == BN && kBLoads * kWaves * 16 == BM, "load split");
   static_assert(BM * BN * 2 <= kLdsBytes, "bf16 output tile must fit the LDS stages");
+  static_assert(kThreads % (BN / 8) == 0, "epilogue rows per pass");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
-// 256 channels x 256 tokens, 8 waves (each 128 channels x 64 tokens).
-using TileBig = Tile<256, 256, 2, 4, 4>;
+// 256 channels x 256 tokens, 4 waves (each 128 x 128 with 32x32x32 MFMAs;
+// the 256 accumulator registers per lane live in AGPRs).
+using TileBig = Tile<256, 256, 2, 2, 32, 4>;
+// 256 x 256, 8 waves (each 128 channels x 64 tokens, 16x16x64 MFMAs).
+using TileBig8 = Tile<256, 256, 2, 4, 16, 4>;
+// 384 channels x 192 tokens, 12 waves (each 96 x 64, 32x32x32 MFMAs, three
+// waves per SIMD).  M = 4608, N = 12288 splits into 768 such tiles: exactly
+// three rounds over 256 CUs, where 256 x 256 tiles leave the fourth round
+// 62 % empty.
+using TileWide = Tile<384, 192, 4, 3, 32, 4>;
 // 128 x 128, 4 waves (each 64 x 64) for layers too small to fill the chip.
-using TileMid = Tile<128, 128, 2, 2, 4>;
+using TileMid = Tile<128, 128, 2, 2, 16, 4>;
+
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// LDS chunk swizzle of row r (rows are 64 bytes = four 16-byte chunks; chunk c
+// of row r is stored at c ^ swz(r)).  On gfx950 a ds_read_b128 is served per
+// half-wave (lanes 0-31, then 32-63) in two 256-byte passes: it runs without
+// bank conflicts when, within each half, every 16-byte slot of a 256-byte
+// window is hit by exactly two lanes (fitted to SQ_LDS_BANK_CONFLICT
+// measurements of fifteen access patterns).  A 16x16x64 fragment half reads
+// rows 0-15 at chunks c and c+1; a 32x32x32 fragment half reads rows 0-31 at
+// one chunk.  Row r sits at slot (r & 3) * 4 + stored chunk, so:
+//   16x16: (r >> 1) & 3 spreads rows {q, q+4, q+8, q+12} x 2 chunks evenly;
+//   32x32: (r >> 2) & 3 spreads rows {q, q+4, ..., q+28} over 4 chunks twice.
+template <int MF>
+__device__ inline int swz(int r) {
+  if constexpr (MF == 16) return (r >> 1) & 3;
+  else return (r >> 2) & 3;
+}
+
+template <int MF> struct Acc;
+template <> struct Acc<16> { using type = v4i; };
+template <> struct Acc<32> { using type = v16i; };
+
+template <int MF>
+__device__ inline typename Acc<MF>::type mfma(v4i a, v4i b, typename Acc<MF>::type c) {
+  if constexpr (MF == 16) return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
 
 // s_waitcnt vmcnt(N) + s_barrier.  lgkmcnt(0) too, so that this wave's LDS
 // reads of the previous slab are complete before anyone refills its stage.
@@ -111,14 +156,14 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hb)) << 16);
 }
 
-__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
 // Byte offset of element (row m, column n) of the bf16 output tile staged in
-// LDS: rows of BN*2 bytes, 16-byte chunks XOR-swizzled by the row.
+// LDS: rows of BN*2 bytes, 16-byte chunks XOR-swizzled by the low 4 bits of
+// the row (stays inside the row for any multiple of 16 chunks).
 template <class T>
 __device__ inline int out_lds_offset(int m, int n) {
-  constexpr int kChunks = T::BN / 8;
-  return m * (T::BN * 2) + ((((n >> 3) ^ m) & (kChunks - 1)) << 4) + ((n & 7) << 1);
+  static_assert(T::BN % 128 == 0, "16-chunk swizzle groups");
+  return m * (T::BN * 2) + (((n >> 3) ^ (m & 15)) << 4) + ((n & 7) << 1);
 }
 
 template <class T, bool DEQUANT>
@@ -149,7 +194,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
     const bool is_a = j < T::kALoads;
     const int i = is_a ? wave * T::kALoads + j : wave * T::kBLoads + (j - T::kALoads);
     const int row = 16 * i + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+    const int chunk = (lane & 3) ^ swz<T::MF>(row);
     if (is_a) {
       src[j] = wq + static_cast<int64_t>(min(n0 + row, N - 1)) * K + chunk * 16;
       dst[j] = i * 16 * kBK;
@@ -170,73 +215,160 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
     }
   };
 
-  // ---- fragment reads: lane reads row (l & 15) of a 16-row block, chunk l >> 4
-  const int frag = (lane & 15) * kBK + ((((lane >> 4) ^ ((lane >> 1) & 3)) & 3) << 4);
-  const int a_base = wn * T::kWaveN * kBK + frag;
-  const int b_base = T::BN * kBK + wm * T::kWaveM * kBK + frag;
+  // ---- fragment reads.  16x16x64: lane reads row (l & 15) of a 16-row block,
+  // chunk l >> 4.  32x32x32: row (l & 31) of a 32-row block, chunk
+  // 2 * kstep + (l >> 5).  Stored chunk = chunk ^ swz(row).
+  constexpr int kRowMask = T::MF - 1;
+  constexpr int kChunkShift = T::MF == 16 ? 4 : 5;
+  const int frow = lane & kRowMask;
+  int frag[T::kKSteps];
+#pragma unroll
+  for (int kk = 0; kk < T::kKSteps; ++kk) {
+    const int chunk = kk * 2 + (lane >> kChunkShift);
+    frag[kk] = frow * kBK + (((chunk ^ swz<T::MF>(frow)) & 3) << 4);
+  }
+  const int a_base = wn * T::kWaveN * kBK;
+  const int b_base = T::BN * kBK + wm * T::kWaveM * kBK;
 
-  v4i acc[T::TN][T::TM];
+  using acc_t = typename Acc<T::MF>::type;
+  acc_t acc[T::TN][T::TM];
 #pragma unroll
   for (int i = 0; i < T::TN; ++i)
 #pragma unroll
-    for (int j = 0; j < T::TM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < T::TM; ++j) acc[i][j] = acc_t{};
+
+  // Token scales of this lane's output columns, fetched before the main loop
+  // so that their latency hides behind it (the dequant epilogue only).
+  float alpha[T::TM];
+  const int m_lane0 = wm * T::kWaveM + (lane & (T::MF - 1));
+#pragma unroll
+  for (int j = 0; j < T::TM; ++j)
+    alpha[j] = DEQUANT ? x_scale[min(m0 + m_lane0 + j * T::MF, M - 1)] : 0.0f;
+
+  // Fragments live in two register sets: while the MFMAs consume slab kt from
+  // one, the LDS reads of slab kt+1 fill the other.  K is a multiple of 128,
+  // so KT is even and the loop runs in pairs with fixed register roles.
+  struct Frags { v4i a[T::kKSteps][T::TN], b[T::kKSteps][T::TM]; };
+  auto read_frags = [&](int slab_stage, Frags& f) {
+    const char* st = lds + slab_stage * T::kStageBytes;
+#pragma unroll
+    for (int kk = 0; kk < T::kKSteps; ++kk) {
+#pragma unroll
+      for (int t = 0; t < T::TM; ++t)
+        f.b[kk][t] = *reinterpret_cast<const v4i*>(st + b_base + t * T::MF * kBK + frag[kk]);
+#pragma unroll
+      for (int t = 0; t < T::TN; ++t)
+        f.a[kk][t] = *reinterpret_cast<const v4i*>(st + a_base + t * T::MF * kBK + frag[kk]);
+    }
+  };
+  auto compute = [&](const Frags& f) {
+#pragma unroll
+    for (int kk = 0; kk < T::kKSteps; ++kk)
+#pragma unroll
+      for (int i = 0; i < T::TN; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TM; ++j) acc[i][j] = mfma<T::MF>(f.a[kk][i], f.b[kk][j], acc[i][j]);
+  };
+  // One pipeline step on slab kt: wait until slab kt+1 has landed (only slab
+  // kt+2 may still be in flight) and everyone is done reading the stage of
+  // slab kt-1, refill that stage with slab kt+3, read slab kt+1's fragments,
+  // then multiply slab kt.  Slab indices past the end re-fetch the last slab
+  // into stages that are never read for results.
+  auto step = [&](int kt, const Frags& cur, Frags& nxt) {
+    wait_vm_barrier<(kStages - 3) * T::kLoads>();
+    issue_slab(min(kt + kStages - 1, KT - 1), (kt + kStages - 1) % kStages);
+    read_frags((kt + 1) % kStages, nxt);
+    compute(cur);
+    // Issue order: every MFMA is followed by one of the step's loads (the
+    // direct-to-LDS loads first, then the LDS fragment reads), so the loads
+    // issue while the matrix unit works instead of in a burst before it.
+    constexpr int kMfmas = T::kKSteps * T::TN * T::TM;
+    constexpr int kReads = T::kKSteps * (T::TN + T::TM);
+    constexpr int kPairV = T::kLoads < kMfmas ? T::kLoads : kMfmas;
+    constexpr int kPairD = kReads < kMfmas - kPairV ? kReads : kMfmas - kPairV;
+#pragma unroll
+    for (int i = 0; i < kPairV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // VMEM (direct-to-LDS load)
+    }
+#pragma unroll
+    for (int i = 0; i < kPairD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+    }
+    if constexpr (kMfmas > kPairV + kPairD)
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - kPairV - kPairD, 0);
+    if constexpr (T::kLoads > kPairV)
+      __builtin_amdgcn_sched_group_barrier(0x010, T::kLoads - kPairV, 0);
+    if constexpr (kReads > kPairD)
+      __builtin_amdgcn_sched_group_barrier(0x100, kReads - kPairD, 0);
+  };
 
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s) issue_slab(min(s, KT - 1), s);
-
-  for (int kt = 0; kt < KT; ++kt) {
-    // slabs kt+1 .. kt+kStages-2 may still be in flight
-    wait_vm_barrier<(kStages - 2) * T::kLoads>();
-    // refill the stage consumed in the previous iteration (slab indices past
-    // the end re-fetch the last slab into a stage that is never read again)
-    issue_slab(min(kt + kStages - 1, KT - 1), (kt + kStages - 1) % kStages);
-
-    const char* st = lds + (kt % kStages) * T::kStageBytes;
-    v4i af[T::TN], bf[T::TM];
-#pragma unroll
-    for (int t = 0; t < T::TN; ++t) af[t] = *reinterpret_cast<const v4i*>(st + a_base + t * 16 * kBK);
-#pragma unroll
-    for (int t = 0; t < T::TM; ++t) bf[t] = *reinterpret_cast<const v4i*>(st + b_base + t * 16 * kBK);
-#pragma unroll
-    for (int i = 0; i < T::TN; ++i)
-#pragma unroll
-      for (int j = 0; j < T::TM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+  Frags f0, f1;
+  wait_vm_barrier<(kStages - 2) * T::kLoads>();
+  read_frags(0, f0);
+  for (int kt = 0; kt < KT; kt += 2) {
+    step(kt, f0, f1);
+    step(kt + 1, f1, f0);
   }
 
-  // lane holds acc[i][j][e] = D[n = n0 + wn*kWaveN + i*16 + 4*(lane/16) + e]
-  //                             [m = m0 + wm*kWaveM + j*16 + lane%16]
-  const int n_loc = wn * T::kWaveN + 4 * (lane >> 4);
-  const int m_loc = wm * T::kWaveM + (lane & 15);
+  // Lane layout of a result block (rows n = weight rows, columns m = tokens):
+  //   16x16: acc[i][j][e]        -> n = i*16 + 4*(l >> 4) + e,           m = j*16 + (l & 15)
+  //   32x32: acc[i][j][4*g + e]  -> n = i*32 + 8*g + 4*(l >> 5) + e,     m = j*32 + (l & 31)
+  // (n and m relative to this wave's corner; e = 0..3 are consecutive n).
+  constexpr int kGroups = T::kAccRegs / 4;
+  const int n_loc = wn * T::kWaveN + 4 * (lane >> kChunkShift);
+  const int m_loc = wm * T::kWaveM + (lane & kRowMask);
 
   if constexpr (DEQUANT) {
     uint16_t* y = static_cast<uint16_t*>(out);
+    // Scales and bias for this lane's outputs: every load is issued before
+    // the first one is used, so their latency is paid once per tile.
     const float sw = *w_scale;
-    float alpha[T::TM];
+    // bias of n = n0 + n_loc + i*MF + 8*g + e, e = 0..3: 8-byte loads when the
+    // four values are in range and aligned, else element by element
+    uint2 bias4[T::TN][kGroups];
+    const bool bias_vec = bias != nullptr && (N & 3) == 0 && (reinterpret_cast<uintptr_t>(bias) & 7) == 0;
 #pragma unroll
-    for (int j = 0; j < T::TM; ++j) {
-      const int m = m0 + m_loc + j * 16;
-      alpha[j] = x_scale[min(m, M - 1)] * sw;
+    for (int i = 0; i < T::TN; ++i) {
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        const int n = n0 + n_loc + i * T::MF + 8 * g;
+        if (bias_vec) {
+          bias4[i][g] = *reinterpret_cast<const uint2*>(bias + min(n, N - 4));
+        } else if (bias != nullptr) {
+          uint32_t h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = bias[min(n + e, N - 1)];
+          bias4[i][g] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        } else {
+          bias4[i][g] = make_uint2(0u, 0u);
+        }
+      }
     }
+#pragma unroll
+    for (int j = 0; j < T::TM; ++j) alpha[j] = alpha[j] * sw;
     // every wave is done with the stages (and every load has landed) before
     // the output tile overwrites them
     wait_vm_barrier<0>();
 #pragma unroll
     for (int i = 0; i < T::TN; ++i) {
-      const int nl = n_loc + i * 16;
-      float b[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int n = min(n0 + nl + e, N - 1);
-        b[e] = bias != nullptr ? bf16_to_f32(bias[n]) : 0.0f;
-      }
+      for (int g = 0; g < kGroups; ++g) {
+        const int nl = n_loc + i * T::MF + 8 * g;
+        const float b[4] = {__uint_as_float(bias4[i][g].x << 16), __uint_as_float(bias4[i][g].x & 0xffff0000u),
+                            __uint_as_float(bias4[i][g].y << 16), __uint_as_float(bias4[i][g].y & 0xffff0000u)};
 #pragma unroll
-      for (int j = 0; j < T::TM; ++j) {
-        float v[4];
+        for (int j = 0; j < T::TM; ++j) {
+          float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(static_cast<float>(acc[i][j][e]), alpha[j], b[e]);
-        *reinterpret_cast<uint2*>(lds + out_lds_offset<T>(m_loc + j * 16, nl)) =
-            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          for (int e = 0; e < 4; ++e)
+            v[e] = __builtin_fmaf(static_cast<float>(acc[i][j][4 * g + e]), alpha[j], b[e]);
+          *reinterpret_cast<uint2*>(lds + out_lds_offset<T>(m_loc + j * T::MF, nl)) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
       }
     }
     __syncthreads();
@@ -266,18 +398,24 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
     const bool vec = (N & 3) == 0;
 #pragma unroll
     for (int i = 0; i < T::TN; ++i) {
-      const int n = n0 + n_loc + i * 16;
 #pragma unroll
-      for (int j = 0; j < T::TM; ++j) {
-        const int m = m0 + m_loc + j * 16;
-        if (m >= M) continue;
-        int32_t* dstp = c + static_cast<int64_t>(m) * N + n;
-        if (vec && n + 3 < N) {
-          *reinterpret_cast<int4*>(dstp) = make_int4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        } else {
+      for (int g = 0; g < kGroups; ++g) {
+        const int n = n0 + n_loc + i * T::MF + 8 * g;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < N) dstp[e] = acc[i][j][e];
+        for (int j = 0; j < T::TM; ++j) {
+          const int m = m0 + m_loc + j * T::MF;
+          if (m >= M) continue;
+          int32_t* dstp = c + static_cast<int64_t>(m) * N + n;
+          const int a0 = acc[i][j][4 * g], a1 = acc[i][j][4 * g + 1];
+          const int a2 = acc[i][j][4 * g + 2], a3 = acc[i][j][4 * g + 3];
+          if (vec && n + 3 < N) {
+            *reinterpret_cast<int4*>(dstp) = make_int4(a0, a1, a2, a3);
+          } else {
+            if (n < N) dstp[0] = a0;
+            if (n + 1 < N) dstp[1] = a1;
+            if (n + 2 < N) dstp[2] = a2;
+            if (n + 3 < N) dstp[3] = a3;
+          }
         }
       }
     }
@@ -297,14 +435,43 @@ hipError_t launch_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
   return hipGetLastError();
 }
 
-// Pick the tile: the large one when it still gives every CU a few tiles.
+// Tile choice: CONVROT_GEMM_TILE=big|big8|wide|mid forces one (the result
+// does not depend on it).  Otherwise: the cost of a large tile is the number
+// of rounds its tiles take over the 256 CUs times the work of one tile; the
+// cheaper of 256x256 and 384x192 wins, and layers with too few large tiles
+// to fill the chip use 128x128.
+int forced_tile() {
+  const char* e = getenv("CONVROT_GEMM_TILE");
+  if (e == nullptr) return 0;
+  if (strcmp(e, "big") == 0) return 1;
+  if (strcmp(e, "big8") == 0) return 2;
+  if (strcmp(e, "mid") == 0) return 3;
+  if (strcmp(e, "wide") == 0) return 4;
+  return 0;
+}
+
+constexpr int64_t kCUs = 256;
+
+int64_t tile_cost(int64_t M, int64_t N, int64_t bn, int64_t bm) {
+  const int64_t tiles = ((N + bn - 1) / bn) * ((M + bm - 1) / bm);
+  return (tiles + kCUs - 1) / kCUs * bn * bm;
+}
+
+int pick_tile(int64_t M, int64_t N) {
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles < 2 * kCUs) return 3;
+  return tile_cost(M, N, 384, 192) < tile_cost(M, N, 256, 256) ? 4 : 1;
+}
+
 template <bool DEQUANT>
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                        const float* w_scale, const uint16_t* bias, void* out, int64_t M,
                        int64_t N, int64_t K, hipStream_t stream) {
-  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles >= 512)
-    return launch_tile<TileBig, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  int t = forced_tile();
+  if (t == 0) t = pick_tile(M, N);
+  if (t == 1) return launch_tile<TileBig, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 2) return launch_tile<TileBig8, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 4) return launch_tile<TileWide, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   return launch_tile<TileMid, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
 }
 
