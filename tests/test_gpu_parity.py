@@ -261,3 +261,28 @@ def test_every_gemm_tile_is_bit_exact(B, tile, M, N, K, monkeypatch):
     acc_ref = oracle.gemm_i32(a, b)
     assert np.array_equal(acc, acc_ref)
     assert np.all(same_bf16(bits_of(y), oracle.epilogue(acc_ref, s_x, s_w, bias)))
+
+
+def test_rotate_quant_exact_ties(B):
+    # g = 256 rotates exactly (1/sqrt(256) = 1/16): with x = H u the rotated
+    # row is 16 u, so with max |u| = 127 the quotient v/s is u itself, and
+    # half-integer entries of u land exactly on rounding ties of the code
+    # (round half to even).  A third entry 0.5 keeps every x = H u entry an
+    # integer or half-integer with at most 8 significant bits (exact in bf16).
+    # The kernel's reciprocal fast path must hand ties to the exact division.
+    g = 256
+    H = oracle.hadamard(g).astype(np.float64)
+    halves = (1.5, 2.5, -3.5, 62.5, -126.5, 0.5)
+    rows = []
+    for half in halves:
+        u = np.zeros(g)
+        u[0], u[7], u[9] = 127.0, half, 0.5
+        rows.append(H @ u)
+    xf = np.tile(np.array(rows), (1, 2))
+    x = synth.to_bf16_bits(xf)
+    assert np.array_equal(oracle.bf16_bits_to_f32(x), xf.astype(np.float32))
+    q, s = B.convrot_rotate_quant(to_dev_bf16(x, DEV), g)
+    q_ref, s_ref = oracle.quant_act(x, g)
+    assert np.array_equal(q.cpu().numpy(), q_ref) and np.array_equal(s.cpu().numpy(), s_ref)
+    assert [int(q_ref[i, 7]) for i in range(len(halves))] == [2, 2, -4, 62, -126, 0]
+    assert all(int(q_ref[i, 9]) == 0 for i in range(len(halves)))
