@@ -49,11 +49,11 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void glb_void_t;
 
-constexpr int kBK = 64;        // bytes of K per LDS stage (one MFMA k step)
-constexpr int kStages = 4;     // LDS stages; slabs are prefetched kStages-1 ahead
+constexpr int kBK = 64;        // bytes of K per LDS stage (one 16x16x64 or two 32x32x32 k steps)
 
-template <int BN_, int BM_, int WN_, int WM_, int MF_, int GROUP_M_>
+template <int BN_, int BM_, int WN_, int WM_, int MF_, int GROUP_M_, int STAGES_ = 4>
 struct Tile {
+  static constexpr int kStages = STAGES_;  // LDS stages; slabs are prefetched kStages-1 ahead
   static constexpr int BN = BN_;          // output channels per workgroup
   static constexpr int BM = BM_;          // tokens per workgroup
   static constexpr int WN = WN_;          // waves along n
@@ -78,6 +78,7 @@ struct Tile {
   static_assert(BM * BN * 2 <= kLdsBytes, "bf16 output tile must fit the LDS stages");
   static_assert(kThreads % (BN / 8) == 0, "epilogue rows per pass");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
+  static_assert(kStages >= 3 && (kStages - 2) * kLoads < 64, "stages / vmcnt range");
 };
 
 // 256 channels x 256 tokens, 4 waves (each 128 x 128 with 32x32x32 MFMAs;
@@ -92,6 +93,10 @@ using TileBig8 = Tile<256, 256, 2, 4, 16, 4>;
 using TileWide = Tile<384, 192, 4, 3, 32, 4>;
 // 128 x 128, 4 waves (each 64 x 64) for layers too small to fill the chip.
 using TileMid = Tile<128, 128, 2, 2, 16, 4>;
+// Few tokens (M <= 32): the weight stream is the whole cost.  32 channels x
+// 32 tokens per one-wave workgroup, so N/32 workgroups stream disjoint weight
+// rows, each with 15 slabs (30 KB) of loads in flight.
+using TileSkinny = Tile<32, 32, 1, 1, 32, 1, 16>;
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 
@@ -158,12 +163,15 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 
 
 // Byte offset of element (row m, column n) of the bf16 output tile staged in
-// LDS: rows of BN*2 bytes, 16-byte chunks XOR-swizzled by the low 4 bits of
-// the row (stays inside the row for any multiple of 16 chunks).
+// LDS: rows of BN*2 bytes, 16-byte chunks XOR-swizzled by the low bits of the
+// row (at most 4 bits, so the XOR stays inside the row for rows of 4 chunks,
+// 8, or any multiple of 16).
 template <class T>
 __device__ inline int out_lds_offset(int m, int n) {
-  static_assert(T::BN % 128 == 0, "16-chunk swizzle groups");
-  return m * (T::BN * 2) + (((n >> 3) ^ (m & 15)) << 4) + ((n & 7) << 1);
+  constexpr int kChunks = T::BN / 8;
+  constexpr int kMask = kChunks >= 16 ? 15 : kChunks - 1;
+  static_assert(kChunks % (kMask + 1) == 0 && (kMask & (kMask + 1)) == 0, "chunk swizzle group");
+  return m * (T::BN * 2) + (((n >> 3) ^ (m & kMask)) << 4) + ((n & 7) << 1);
 }
 
 template <class T, bool DEQUANT>
@@ -275,9 +283,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
   // then multiply slab kt.  Slab indices past the end re-fetch the last slab
   // into stages that are never read for results.
   auto step = [&](int kt, const Frags& cur, Frags& nxt) {
-    wait_vm_barrier<(kStages - 3) * T::kLoads>();
-    issue_slab(min(kt + kStages - 1, KT - 1), (kt + kStages - 1) % kStages);
-    read_frags((kt + 1) % kStages, nxt);
+    wait_vm_barrier<(T::kStages - 3) * T::kLoads>();
+    issue_slab(min(kt + T::kStages - 1, KT - 1), (kt + T::kStages - 1) % T::kStages);
+    read_frags((kt + 1) % T::kStages, nxt);
     compute(cur);
     // Issue order: every MFMA is followed by one of the step's loads (the
     // direct-to-LDS loads first, then the LDS fragment reads), so the loads
@@ -305,9 +313,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
   };
 
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue_slab(min(s, KT - 1), s);
+  for (int s = 0; s < T::kStages - 1; ++s) issue_slab(min(s, KT - 1), s);
   Frags f0, f1;
-  wait_vm_barrier<(kStages - 2) * T::kLoads>();
+  wait_vm_barrier<(T::kStages - 2) * T::kLoads>();
   read_frags(0, f0);
   for (int kt = 0; kt < KT; kt += 2) {
     step(kt, f0, f1);
@@ -435,11 +443,12 @@ hipError_t launch_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
   return hipGetLastError();
 }
 
-// Tile choice: CONVROT_GEMM_TILE=big|big8|wide|mid forces one (the result
-// does not depend on it).  Otherwise: the cost of a large tile is the number
-// of rounds its tiles take over the 256 CUs times the work of one tile; the
-// cheaper of 256x256 and 384x192 wins, and layers with too few large tiles
-// to fill the chip use 128x128.
+// Tile choice: CONVROT_GEMM_TILE=big|big8|wide|mid|skinny forces one (the
+// result does not depend on it).  Otherwise: M <= 32 streams the weight with
+// the skinny tile; layers with fewer than 64 large tiles use 128x128; else
+// the cost of a large tile is the number of rounds its tiles take over the
+// 256 CUs times the work of one tile, and the cheaper of 256x256 and 384x192
+// wins.
 int forced_tile() {
   const char* e = getenv("CONVROT_GEMM_TILE");
   if (e == nullptr) return 0;
@@ -447,6 +456,7 @@ int forced_tile() {
   if (strcmp(e, "big8") == 0) return 2;
   if (strcmp(e, "mid") == 0) return 3;
   if (strcmp(e, "wide") == 0) return 4;
+  if (strcmp(e, "skinny") == 0) return 5;
   return 0;
 }
 
@@ -458,8 +468,9 @@ int64_t tile_cost(int64_t M, int64_t N, int64_t bn, int64_t bm) {
 }
 
 int pick_tile(int64_t M, int64_t N) {
+  if (M <= 32) return 5;
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles < 2 * kCUs) return 3;
+  if (big_tiles < 64) return 3;   // tiny layers: more, smaller tiles
   return tile_cost(M, N, 384, 192) < tile_cost(M, N, 256, 256) ? 4 : 1;
 }
 
@@ -472,6 +483,7 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
   if (t == 1) return launch_tile<TileBig, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 2) return launch_tile<TileBig8, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 4) return launch_tile<TileWide, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 5) return launch_tile<TileSkinny, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   return launch_tile<TileMid, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
 }
 
