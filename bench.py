@@ -1,11 +1,11 @@
 #!/usr/bin/env python3
 """Throughput of the INT8 ConvRot linear layer on one MI355X.
 
-One step = one pass of the layer's hot path over one batch of tokens:
-rotate + per-token int8 quantization of the bf16 activation (one kernel),
-then the int8 x int8 -> int32 MFMA GEMM with the fused dequant + bias bf16
-epilogue (one kernel) -- exactly the two launches convrot_linear makes for a
-batch of at most 2N tokens.  The weight is prepared once beforehand, as the
+One step = one convrot_linear call: one pass of the layer's hot path over one
+batch of tokens -- rotate + per-token int8 quantization of the bf16
+activation (one kernel), then the int8 x int8 -> int32 MFMA GEMM with the
+fused dequant + bias bf16 epilogue (one kernel); the batch is at most 2N
+tokens, so it is one slice.  The weight is prepared once beforehand, as the
 pages' checkpoints ship it already rotated and quantized.  Inputs are seeded
 synthetic tensors resident in HBM before the timed region starts.
 
@@ -15,7 +15,8 @@ outlier channels up to x50.
 
 Printed: one JSON line with the metric (int8 TOPS = 2*M*N*K / step time), the
 roofline of the dominant kernel (the GEMM, timed with HIP events on the stream
-it runs on) and the CPU oracle timed on a bounded sample of token rows.
+it runs on over K back-to-back launches right after the timed steps) and the
+CPU oracle timed on a bounded sample of token rows.
 """
 import argparse
 import hashlib
@@ -37,7 +38,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--group", type=int, default=128, choices=(128, 256))
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample (0 disables the cpu_baseline leg)")
@@ -130,41 +131,47 @@ def main():
     s = torch.empty(M, dtype=torch.float32, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(binding.convrot_linear_workspace(M, K, N), dtype=torch.uint8, device=dev)
-    assert binding.convrot_linear_workspace(M, K, N) >= M * K   # one slice: same two launches
+    assert binding.convrot_linear_workspace(M, K, N) >= M * K   # one slice: two launches per call
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        binding.convrot_rotate_quant(x, g, q, s)
-        binding.convrot_gemm_dequant(q, s, wq, s_w, bias, out=y)
+        binding.convrot_linear(x, wq, s_w, g, bias, out=y, workspace=ws)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps; HIP events on the launch stream bracket every GEMM
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # timed region: K steps bracketed by synchronize (wall clock) and by HIP
+    # events recorded on the launch stream
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        binding.convrot_rotate_quant(x, g, q, s)
-        ev[i][0].record(stream)
-        binding.convrot_gemm_dequant(q, s, wq, s_w, bias, out=y)
-        ev[i][1].record(stream)
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        step()
+    ev[1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
-    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    step_ms_events = ev[0].elapsed_time(ev[1]) / args.steps
 
-    # convrot_linear itself (same kernels, one C call), for reference
-    for _ in range(3):
-        binding.convrot_linear(x, wq, s_w, g, bias, out=y, workspace=ws)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
+    # the dominant kernel (GEMM + epilogue) on its own: K back-to-back launches
+    # on the same stream between one pair of HIP events, so the per-launch time
+    # carries no event overhead (an event pair around every launch adds ~10 us)
+    binding.convrot_rotate_quant(x, g, q, s)
+    ev[2].record(stream)
     for _ in range(args.steps):
-        binding.convrot_linear(x, wq, s_w, g, bias, out=y, workspace=ws)
+        binding.convrot_gemm_dequant(q, s, wq, s_w, bias, out=y)
+    ev[3].record(stream)
     torch.cuda.synchronize()
-    linear_s = (time.perf_counter() - t2) / args.steps
+    gemm_ms = ev[2].elapsed_time(ev[3]) / args.steps
+    # and the rotate+quant kernel the same way
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        binding.convrot_rotate_quant(x, g, q, s)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    rotq_ms = ev[0].elapsed_time(ev[1]) / args.steps
 
     ops = 2.0 * M * N * K
     value = ops / step_s / 1e12
@@ -188,7 +195,8 @@ def main():
                                f"with outlier channels up to x50, bf16 bias",
                    "M": M, "K": K, "N": N, "group": g, "parallelism": "single GPU"},
         "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
-        "convrot_linear_ms": round(linear_s * 1e3, 5),
+        "ms_per_step_events": round(step_ms_events, 5),
+        "rotate_quant_ms": round(rotq_ms, 5),
         "roofline": {"bound": "mfma", "kernel": "gemm_i8_kernel (GEMM + dequant/bias epilogue)",
                      "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                      "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
