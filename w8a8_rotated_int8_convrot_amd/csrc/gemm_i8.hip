@@ -8,22 +8,29 @@
 //   y[m][n]   = bf16_rne(fmaf((float)acc, x_scale[m] * w_scale, bias[n]))
 //
 // Design for CDNA4:
-//  * v_mfma_i32_16x16x64_i8.  The weight tile is the instruction's A operand
-//    and the activation tile its B operand, so a lane's 16x16 result block
-//    holds four consecutive output channels n of one token m.
+//  * v_mfma_i32_32x32x32_i8 (v_mfma_i32_16x16x64_i8 in the 8-wave and small
+//    tiles).  The weight tile is the instruction's A operand and the
+//    activation tile its B operand, so a lane's result block holds four
+//    consecutive output channels n of one token m.
 //  * Both operands are K-contiguous in HBM ([N, K] weight as stored by
-//    nn.Linear, [M, K] codes), so an A or B fragment is 16 rows x 16
-//    consecutive bytes: one ds_read_b128 per lane.  Which bytes of a 64-byte k
-//    step a lane supplies does not matter for an integer dot product as long
-//    as both operands use the same mapping, and they do.
+//    nn.Linear, [M, K] codes), so an A or B fragment is MF rows x 16
+//    consecutive bytes: one ds_read_b128 per lane.  Which bytes of a k step
+//    a lane supplies does not matter for an integer dot product as long as
+//    both operands use the same mapping, and they do.
 //  * Global -> LDS by direct-to-LDS loads (global_load_lds_dwordx4: each
-//    wave instruction fills 1 KB = 16 LDS rows of 64 bytes, no registers
-//    involved), four LDS stages of one 64-byte k slab each, prefetched three
-//    slabs ahead.  A slab's fragments are read into registers one step before
-//    its MFMAs run (two register sets), after `s_waitcnt vmcnt` (this wave's
-//    loads of that slab have landed) and one `s_barrier` (so have everyone
-//    else's, and everyone is done with the stage about to be refilled).
-//  * LDS rows are 64 bytes; the four 16-byte chunks of a row are stored
+//    wave instruction fills 1 KB of LDS rows, no registers involved).  A
+//    "slab" is BK bytes of K of both operand tiles.  Two pipelines:
+//    - BK = 128, two stages (the default 384 x 192 tile): the slab after
+//      next is issued at each slab boundary into the stage just finished; a
+//      row's 128 bytes are one request, which halves the L1 -> L2 request
+//      count of 64-byte slabs, and there is one barrier per 128 bytes of K;
+//    - BK = 64, three or more stages, prefetched kStages-1 slabs ahead.
+//    Fragments are double-buffered per MFMA k step: while one k step's MFMAs
+//    run from one register set, the LDS reads of the next fill the other.
+//    Stage reuse is guarded by `s_waitcnt vmcnt` (this wave's loads of the
+//    needed slab have landed) and one `s_barrier` (so have everyone else's,
+//    and everyone is done with the stage about to be refilled).
+//  * LDS rows are BK bytes; the 16-byte chunks of a row are stored
 //    XOR-swizzled by row bits (swz below), so the lanes served together by
 //    one ds_read_b128 pass fall into distinct banks.  A lane's direct-to-LDS
 //    slot is fixed by its lane id, so the swizzle is applied by choosing
@@ -39,6 +46,7 @@
 //    results are discarded) and stores are masked; K is a multiple of 128.
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "convrot_internal.hpp"
 
@@ -49,11 +57,12 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void glb_void_t;
 
-constexpr int kBK = 64;        // bytes of K per LDS stage (one 16x16x64 or two 32x32x32 k steps)
-
-template <int BN_, int BM_, int WN_, int WM_, int MF_, int GROUP_M_, int STAGES_ = 4>
+template <int BN_, int BM_, int WN_, int WM_, int MF_, int GROUP_M_, int STAGES_ = 4, int BK_ = 64>
 struct Tile {
   static constexpr int kStages = STAGES_;  // LDS stages; slabs are prefetched kStages-1 ahead
+  static constexpr int BK = BK_;           // bytes of K per LDS stage (a "slab")
+  static constexpr int kRowChunks = BK / 16;       // 16-byte chunks per LDS row
+  static constexpr int kRowsPerLoad = 64 / kRowChunks;   // LDS rows one direct-to-LDS instruction fills
   static constexpr int BN = BN_;          // output channels per workgroup
   static constexpr int BM = BM_;          // tokens per workgroup
   static constexpr int WN = WN_;          // waves along n
@@ -64,21 +73,26 @@ struct Tile {
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kWaveN = BN / WN, kWaveM = BM / WM;
   static constexpr int TN = kWaveN / MF, TM = kWaveM / MF;   // MFMA blocks per wave
-  static constexpr int kKSteps = MF == 16 ? 1 : 2;           // MFMA k steps per 64-byte slab
+  static constexpr int kUnitBytes = MF == 16 ? 64 : 32;     // K bytes of one MFMA
+  static constexpr int kKSteps = BK / kUnitBytes;            // MFMA k steps per slab
   static constexpr int kAccRegs = MF == 16 ? 4 : 16;
-  static constexpr int kStageBytes = (BN + BM) * kBK;
+  static constexpr int kStageBytes = (BN + BM) * BK;
   static constexpr int kLdsBytes = kStages * kStageBytes;
   // direct-to-LDS instructions per wave and slab (each moves 16 rows)
-  static constexpr int kALoads = BN / 16 / kWaves;
-  static constexpr int kBLoads = BM / 16 / kWaves;
+  static constexpr int kALoads = BN / kRowsPerLoad / kWaves;
+  static constexpr int kBLoads = BM / kRowsPerLoad / kWaves;
   static constexpr int kLoads = kALoads + kBLoads;
   static_assert(MF == 16 || MF == 32, "MFMA shape");
   static_assert(BN % (WN * MF) == 0 && BM % (WM * MF) == 0, "wave tile");
-  static_assert(kALoads * kWaves * 16 == BN && kBLoads * kWaves * 16 == BM, "load split");
+  static_assert(BK == 64 || BK == 128, "slab width");
+  static_assert(kALoads * kWaves * kRowsPerLoad == BN && kBLoads * kWaves * kRowsPerLoad == BM,
+                "load split");
   static_assert(BM * BN * 2 <= kLdsBytes, "bf16 output tile must fit the LDS stages");
   static_assert(kThreads % (BN / 8) == 0, "epilogue rows per pass");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
-  static_assert(kStages >= 3 && (kStages - 2) * kLoads < 64, "stages / vmcnt range");
+  // two stages (double buffering, the slab after next issued at each slab
+  // boundary) or three and more (prefetched kStages-1 slabs ahead)
+  static_assert(kStages >= 2 && (kStages - 2) * kLoads < 64 && kLoads < 64, "stages / vmcnt range");
 };
 
 // 256 channels x 256 tokens, 4 waves (each 128 x 128 with 32x32x32 MFMAs;
@@ -97,6 +111,10 @@ using TileMid = Tile<128, 128, 2, 2, 16, 4>;
 // 32 tokens per one-wave workgroup, so N/32 workgroups stream disjoint weight
 // rows, each with 15 slabs (30 KB) of loads in flight.
 using TileSkinny = Tile<32, 32, 1, 1, 32, 1, 16>;
+// 384 x 192 as TileWide, but 128-byte slabs in two stages: one barrier per
+// 128 bytes of K, and the direct-to-LDS loads fetch 128 contiguous bytes of
+// a row (eight lanes) per request instead of 64.
+using TileWide128 = Tile<384, 192, 4, 3, 32, 4, 2, 128>;
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 
@@ -110,9 +128,13 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 // one chunk.  Row r sits at slot (r & 3) * 4 + stored chunk, so:
 //   16x16: (r >> 1) & 3 spreads rows {q, q+4, q+8, q+12} x 2 chunks evenly;
 //   32x32: (r >> 2) & 3 spreads rows {q, q+4, ..., q+28} over 4 chunks twice.
-template <int MF>
+// With 128-byte rows (eight chunks) row r sits at slot (r & 1) * 8 + stored
+// chunk, and (r >> 1) & 7 gives each of the 16 slots exactly two of the 32
+// rows of a 32x32 half (or of the 16 rows x 2 chunks of a 16x16 half).
+template <int MF, int BK>
 __device__ inline int swz(int r) {
-  if constexpr (MF == 16) return (r >> 1) & 3;
+  if constexpr (BK == 128) return (r >> 1) & 7;
+  else if constexpr (MF == 16) return (r >> 1) & 3;
   else return (r >> 2) & 3;
 }
 
@@ -201,20 +223,20 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
   for (int j = 0; j < T::kLoads; ++j) {
     const bool is_a = j < T::kALoads;
     const int i = is_a ? wave * T::kALoads + j : wave * T::kBLoads + (j - T::kALoads);
-    const int row = 16 * i + (lane >> 2);
-    const int chunk = (lane & 3) ^ swz<T::MF>(row);
+    const int row = T::kRowsPerLoad * i + lane / T::kRowChunks;
+    const int chunk = (lane % T::kRowChunks) ^ swz<T::MF, T::BK>(row);
     if (is_a) {
       src[j] = wq + static_cast<int64_t>(min(n0 + row, N - 1)) * K + chunk * 16;
-      dst[j] = i * 16 * kBK;
+      dst[j] = i * T::kRowsPerLoad * T::BK;
     } else {
       src[j] = xq + static_cast<int64_t>(min(m0 + row, M - 1)) * K + chunk * 16;
-      dst[j] = T::BN * kBK + i * 16 * kBK;
+      dst[j] = T::BN * T::BK + i * T::kRowsPerLoad * T::BK;
     }
   }
-  const int KT = K / kBK;
+  const int KT = K / T::BK;
 
   auto issue_slab = [&](int slab, int stage) {
-    const int64_t k0 = static_cast<int64_t>(slab) * kBK;
+    const int64_t k0 = static_cast<int64_t>(slab) * T::BK;
 #pragma unroll
     for (int j = 0; j < T::kLoads; ++j) {
       __builtin_amdgcn_global_load_lds((glb_void_t*)(src[j] + k0),
@@ -232,11 +254,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
   int frag[T::kKSteps];
 #pragma unroll
   for (int kk = 0; kk < T::kKSteps; ++kk) {
-    const int chunk = kk * 2 + (lane >> kChunkShift);
-    frag[kk] = frow * kBK + (((chunk ^ swz<T::MF>(frow)) & 3) << 4);
+    const int chunk = kk * (T::kUnitBytes / 16) + (lane >> kChunkShift);
+    frag[kk] = frow * T::BK + (((chunk ^ swz<T::MF, T::BK>(frow)) & (T::kRowChunks - 1)) << 4);
   }
-  const int a_base = wn * T::kWaveN * kBK;
-  const int b_base = T::BN * kBK + wm * T::kWaveM * kBK;
+  const int a_base = wn * T::kWaveN * T::BK;
+  const int b_base = T::BN * T::BK + wm * T::kWaveM * T::BK;
 
   using acc_t = typename Acc<T::MF>::type;
   acc_t acc[T::TN][T::TM];
@@ -253,47 +275,37 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
   for (int j = 0; j < T::TM; ++j)
     alpha[j] = DEQUANT ? x_scale[min(m0 + m_lane0 + j * T::MF, M - 1)] : 0.0f;
 
-  // Fragments live in two register sets: while the MFMAs consume slab kt from
-  // one, the LDS reads of slab kt+1 fill the other.  K is a multiple of 128,
-  // so KT is even and the loop runs in pairs with fixed register roles.
-  struct Frags { v4i a[T::kKSteps][T::TN], b[T::kKSteps][T::TM]; };
-  auto read_frags = [&](int slab_stage, Frags& f) {
+  // Fragments are double-buffered per MFMA k step (a "unit": 32 bytes of K
+  // for 32x32x32, 64 for 16x16x64): while the MFMAs of one unit run from one
+  // register set, the LDS reads of the next unit fill the other.  Only two
+  // units' fragments are ever live, which keeps the 12-wave tile within its
+  // 168 registers.  The unit after the last of slab kt is the first of slab
+  // kt+1, which the barrier at the top of step kt has made visible.
+  struct KFrag { v4i a[T::TN], b[T::TM]; };
+  auto read_unit = [&](int slab_stage, int kk, KFrag& f) {
     const char* st = lds + slab_stage * T::kStageBytes;
 #pragma unroll
-    for (int kk = 0; kk < T::kKSteps; ++kk) {
+    for (int t = 0; t < T::TM; ++t)
+      f.b[t] = *reinterpret_cast<const v4i*>(st + b_base + t * T::MF * T::BK + frag[kk]);
 #pragma unroll
-      for (int t = 0; t < T::TM; ++t)
-        f.b[kk][t] = *reinterpret_cast<const v4i*>(st + b_base + t * T::MF * kBK + frag[kk]);
-#pragma unroll
-      for (int t = 0; t < T::TN; ++t)
-        f.a[kk][t] = *reinterpret_cast<const v4i*>(st + a_base + t * T::MF * kBK + frag[kk]);
-    }
+    for (int t = 0; t < T::TN; ++t)
+      f.a[t] = *reinterpret_cast<const v4i*>(st + a_base + t * T::MF * T::BK + frag[kk]);
   };
-  auto compute = [&](const Frags& f) {
+  auto compute_unit = [&](const KFrag& f) {
 #pragma unroll
-    for (int kk = 0; kk < T::kKSteps; ++kk)
+    for (int i = 0; i < T::TN; ++i)
 #pragma unroll
-      for (int i = 0; i < T::TN; ++i)
-#pragma unroll
-        for (int j = 0; j < T::TM; ++j) acc[i][j] = mfma<T::MF>(f.a[kk][i], f.b[kk][j], acc[i][j]);
+      for (int j = 0; j < T::TM; ++j) acc[i][j] = mfma<T::MF>(f.a[i], f.b[j], acc[i][j]);
   };
-  // One pipeline step on slab kt: wait until slab kt+1 has landed (only slab
-  // kt+2 may still be in flight) and everyone is done reading the stage of
-  // slab kt-1, refill that stage with slab kt+3, read slab kt+1's fragments,
-  // then multiply slab kt.  Slab indices past the end re-fetch the last slab
-  // into stages that are never read for results.
-  auto step = [&](int kt, const Frags& cur, Frags& nxt) {
-    wait_vm_barrier<(T::kStages - 3) * T::kLoads>();
-    issue_slab(min(kt + T::kStages - 1, KT - 1), (kt + T::kStages - 1) % T::kStages);
-    read_frags((kt + 1) % T::kStages, nxt);
-    compute(cur);
-    // Issue order: every MFMA is followed by one of the step's loads (the
-    // direct-to-LDS loads first, then the LDS fragment reads), so the loads
-    // issue while the matrix unit works instead of in a burst before it.
-    constexpr int kMfmas = T::kKSteps * T::TN * T::TM;
-    constexpr int kReads = T::kKSteps * (T::TN + T::TM);
-    constexpr int kPairV = T::kLoads < kMfmas ? T::kLoads : kMfmas;
-    constexpr int kPairD = kReads < kMfmas - kPairV ? kReads : kMfmas - kPairV;
+  // Issue order inside a unit: each MFMA is followed by one of the unit's
+  // loads (direct-to-LDS loads first, then LDS fragment reads), so the loads
+  // issue while the matrix unit works instead of in a burst before it.
+  constexpr int kUnitMfmas = T::TN * T::TM;
+  constexpr int kUnitReads = T::TN + T::TM;
+  auto order_unit = [&](auto loads_c) {
+    constexpr int kV = decltype(loads_c)::value;
+    constexpr int kPairV = kV < kUnitMfmas ? kV : kUnitMfmas;
+    constexpr int kPairD = kUnitReads < kUnitMfmas - kPairV ? kUnitReads : kUnitMfmas - kPairV;
 #pragma unroll
     for (int i = 0; i < kPairV; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
@@ -304,22 +316,105 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
     }
-    if constexpr (kMfmas > kPairV + kPairD)
-      __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - kPairV - kPairD, 0);
-    if constexpr (T::kLoads > kPairV)
-      __builtin_amdgcn_sched_group_barrier(0x010, T::kLoads - kPairV, 0);
-    if constexpr (kReads > kPairD)
-      __builtin_amdgcn_sched_group_barrier(0x100, kReads - kPairD, 0);
+    if constexpr (kUnitMfmas > kPairV + kPairD)
+      __builtin_amdgcn_sched_group_barrier(0x008, kUnitMfmas - kPairV - kPairD, 0);
+    if constexpr (kV > kPairV) __builtin_amdgcn_sched_group_barrier(0x010, kV - kPairV, 0);
+    if constexpr (kUnitReads > kPairD)
+      __builtin_amdgcn_sched_group_barrier(0x100, kUnitReads - kPairD, 0);
+    __builtin_amdgcn_sched_barrier(0);   // nothing crosses into the next unit
+  };
+  // Slab-boundary unit of the two-stage pipeline: its MFMAs carry all of the
+  // next slab's direct-to-LDS loads and the next unit's fragment reads, one
+  // of each after every MFMA.
+  auto order_boundary = [&]() {
+    constexpr int kV = T::kLoads;
+    constexpr int kT = kV < kUnitReads ? (kV < kUnitMfmas ? kV : kUnitMfmas)
+                                       : (kUnitReads < kUnitMfmas ? kUnitReads : kUnitMfmas);
+#pragma unroll
+    for (int i = 0; i < kT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // VMEM (direct-to-LDS load)
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+    }
+    if constexpr (kUnitMfmas > kT) __builtin_amdgcn_sched_group_barrier(0x008, kUnitMfmas - kT, 0);
+    if constexpr (kV > kT) __builtin_amdgcn_sched_group_barrier(0x010, kV - kT, 0);
+    if constexpr (kUnitReads > kT) __builtin_amdgcn_sched_group_barrier(0x100, kUnitReads - kT, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // One pipeline step on slab kt (x holds its first unit on entry; on exit
+  // the register set named by the return value holds slab kt+1's first
+  // unit): wait until slab kt+1 has landed (only slab kt+2 may still be in
+  // flight) and everyone is done reading the stage of slab kt-1, refill that
+  // stage with slab kt+3, then run the slab's units.  Slab indices past the
+  // end re-fetch the last slab into stages that are never read for results.
+  auto step = [&](int kt, KFrag& x, KFrag& y) {
+    wait_vm_barrier<(T::kStages >= 3 ? (T::kStages - 3) * T::kLoads : 0)>();
+    issue_slab(min(kt + T::kStages - 1, KT - 1), (kt + T::kStages - 1) % T::kStages);
+    if constexpr (T::kKSteps == 2) {
+      read_unit(kt % T::kStages, 1, y);
+      compute_unit(x);
+      order_unit(std::integral_constant<int, T::kLoads>{});
+      read_unit((kt + 1) % T::kStages, 0, x);
+      compute_unit(y);
+      order_unit(std::integral_constant<int, 0>{});
+    } else {
+      read_unit((kt + 1) % T::kStages, 0, y);
+      compute_unit(x);
+      order_unit(std::integral_constant<int, T::kLoads>{});
+    }
   };
 
 #pragma unroll
   for (int s = 0; s < T::kStages - 1; ++s) issue_slab(min(s, KT - 1), s);
-  Frags f0, f1;
-  wait_vm_barrier<(T::kStages - 2) * T::kLoads>();
-  read_frags(0, f0);
-  for (int kt = 0; kt < KT; kt += 2) {
-    step(kt, f0, f1);
-    step(kt + 1, f1, f0);
+  KFrag f0, f1;
+  if constexpr (T::kStages == 2) {
+    // Two stages: slab kt+2 is issued at the boundary between slabs kt and
+    // kt+1, into the stage slab kt occupied; by then slab kt+1 has landed and
+    // every wave holds slab kt's last unit in registers.  Units alternate
+    // between the register sets (an even count per slab, so every slab starts
+    // in f0).
+    static_assert(T::kKSteps % 2 == 0, "even unit count per slab");
+    issue_slab(0, 0);
+    issue_slab(min(1, KT - 1), 1);
+    wait_vm_barrier<T::kLoads>();      // slab 0 has landed, slab 1 may be in flight
+    read_unit(0, 0, f0);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int st = kt & 1;
+#pragma unroll
+      for (int u = 0; u + 2 < T::kKSteps; u += 2) {
+        read_unit(st, u + 1, f1);
+        compute_unit(f0);
+        order_unit(std::integral_constant<int, 0>{});
+        read_unit(st, u + 2, f0);
+        compute_unit(f1);
+        order_unit(std::integral_constant<int, 0>{});
+      }
+      read_unit(st, T::kKSteps - 1, f1);
+      compute_unit(f0);
+      order_unit(std::integral_constant<int, 0>{});
+      // slab boundary (slab indices past the end re-fetch the last slab into
+      // a stage that is never read for results)
+      wait_vm_barrier<0>();
+      issue_slab(min(kt + 2, KT - 1), st);
+      read_unit(st ^ 1, 0, f0);
+      compute_unit(f1);
+      order_boundary();
+    }
+  } else {
+    static_assert(T::kKSteps <= 2, "three-plus stage pipeline runs one or two units per slab");
+    wait_vm_barrier<(T::kStages - 2) * T::kLoads>();
+    read_unit(0, 0, f0);
+    // K is a multiple of 128, so KT is even and the loop runs in slab pairs
+    // with fixed register roles.
+    for (int kt = 0; kt < KT; kt += 2) {
+      if constexpr (T::kKSteps == 2) {
+        step(kt, f0, f1);       // f0 <- first unit of slab kt+1
+        step(kt + 1, f0, f1);
+      } else {
+        step(kt, f0, f1);       // f1 <- slab kt+1
+        step(kt + 1, f1, f0);
+      }
+    }
   }
 
   // Lane layout of a result block (rows n = weight rows, columns m = tokens):
@@ -457,6 +552,7 @@ int forced_tile() {
   if (strcmp(e, "mid") == 0) return 3;
   if (strcmp(e, "wide") == 0) return 4;
   if (strcmp(e, "skinny") == 0) return 5;
+  if (strcmp(e, "wide128") == 0) return 6;
   return 0;
 }
 
@@ -471,7 +567,7 @@ int pick_tile(int64_t M, int64_t N) {
   if (M <= 32) return 5;
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles < 64) return 3;   // tiny layers: more, smaller tiles
-  return tile_cost(M, N, 384, 192) < tile_cost(M, N, 256, 256) ? 4 : 1;
+  return tile_cost(M, N, 384, 192) < tile_cost(M, N, 256, 256) ? 6 : 1;
 }
 
 template <bool DEQUANT>
@@ -484,6 +580,7 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
   if (t == 2) return launch_tile<TileBig8, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 4) return launch_tile<TileWide, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 5) return launch_tile<TileSkinny, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 6) return launch_tile<TileWide128, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   return launch_tile<TileMid, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
 }
 
