@@ -16,7 +16,14 @@ outlier channels up to x50.
 Printed: one JSON line with the metric (int8 TOPS = 2*M*N*K / step time), the
 roofline of the dominant kernel (the GEMM, timed with HIP events on the stream
 it runs on over K back-to-back launches right after the timed steps) and the
-CPU oracle timed on a bounded sample of token rows.
+CPU oracle timed on a bounded sample of token rows.  Beside them:
+  mfma_ceiling  the rate a register-only MFMA loop sustains on this machine
+                with this workload's own int8 codes (the board's power limit
+                lowers the clock with operand toggling), and the GEMM's
+                fraction of it;
+  paths         the HBM-bound steps against 8 TB/s: rotate+quant of this
+                workload, and the few-token layer (M=16, K=4096, N=12288)
+                with its weight read from HBM on every call.
 """
 import argparse
 import hashlib
@@ -103,6 +110,50 @@ def cpu_baseline(L, budget_s):
                       f"{t_used:.1f} s, single-threaded C oracle"}
 
 
+def small_m_paths(binding, synth, np, torch, dev, stream, g, steps):
+    """The few-token case (M=16, K=4096, N=12288), which streams the weight:
+    GEMM+epilogue and the whole layer timed over 8 copies of the prepared
+    weight in turn (403 MB, more than the 256 MB last-level cache), so every
+    call reads its weight from HBM."""
+    L = synth.make_layer("small_m", g=g)
+    M, K, N = L.M, L.K, L.N
+    x = torch.from_numpy(L.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    bias = torch.from_numpy(L.bias_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    wq, s_w = binding.convrot_prepare_weight(torch.from_numpy(L.w).to(dev), g)
+    copies = [wq] + [wq.clone() for _ in range(7)]
+    q, s = binding.convrot_rotate_quant(x, g)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(binding.convrot_linear_workspace(M, K, N), dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    n = max(steps, 16)
+
+    def timed(fn):
+        for i in range(8):
+            fn(copies[i])
+        ev[0].record(stream)
+        for i in range(n):
+            fn(copies[i % 8])
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / n
+
+    gemm_ms = timed(lambda w: binding.convrot_gemm_dequant(q, s, w, s_w, bias, out=y))
+    lin_ms = timed(lambda w: binding.convrot_linear(x, w, s_w, g, bias, out=y, workspace=ws))
+    gemm_bytes = N * K + M * K + 2 * M * N + 2 * N + 4 * M
+    lin_bytes = gemm_bytes + 3 * M * K + 4 * M
+    wl = f"M={M} tokens, K={K}, N={N}, group {g}, weight read from HBM (8 rotating copies)"
+    return {
+        "small_m_gemm": {"kernel": "gemm_i8_kernel (skinny tile)", "workload": wl, "bound": "hbm",
+                         "ms": round(gemm_ms, 5), "bytes": gemm_bytes,
+                         "achieved": round(gemm_bytes / (gemm_ms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gemm_bytes / (gemm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "small_m_linear": {"workload": wl, "ms": round(lin_ms, 5), "bytes": lin_bytes,
+                           "achieved": round(lin_bytes / (lin_ms * 1e-3) / 1e9, 1),
+                           "unit": "GB/s"},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -173,6 +224,22 @@ def main():
     torch.cuda.synchronize()
     rotq_ms = ev[0].elapsed_time(ev[1]) / args.steps
 
+    # the matrix cores' own ceiling on this machine and this data: a
+    # register-only MFMA loop fed with the layer's activation and weight codes
+    probe_blocks, probe_iters = 1024, 1400
+    probe_out = torch.empty(probe_blocks * 256, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        binding.convrot_probe_mfma_i8(q, wq, probe_blocks, probe_iters, out=probe_out)
+    ev[0].record(stream)
+    for _ in range(5):
+        binding.convrot_probe_mfma_i8(q, wq, probe_blocks, probe_iters, out=probe_out)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    probe_ms = ev[0].elapsed_time(ev[1]) / 5
+    probe_tops = probe_blocks * 4 * probe_iters * 16 * 65536 / (probe_ms * 1e-3) / 1e12
+
+    small = small_m_paths(binding, synth, np, torch, dev, stream, g, args.steps)
+
     ops = 2.0 * M * N * K
     value = ops / step_s / 1e12
     achieved = ops / (gemm_ms * 1e-3) / 1e12
@@ -201,6 +268,20 @@ def main():
                      "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                      "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
                      "gemm_ms": round(gemm_ms, 5)},
+    }
+    rq_bytes = 3 * M * K + 4 * M          # bf16 in, int8 codes + fp32 scales out
+    out["mfma_ceiling"] = {
+        "kernel": "register-only v_mfma_i32_32x32x32_i8 loop (convrot_probe_mfma_i8) on this "
+                  "workload's activation and weight codes",
+        "achieved": round(probe_tops, 1), "unit": "TOPS",
+        "gemm_frac_of_ceiling": round(achieved / probe_tops, 4)}
+    out["paths"] = {
+        "rotate_quant": {"kernel": "rotq_block_kernel", "bound": "hbm", "ms": round(rotq_ms, 5),
+                         "bytes": rq_bytes,
+                         "achieved": round(rq_bytes / (rotq_ms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(rq_bytes / (rotq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        **small,
     }
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)

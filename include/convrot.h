@@ -143,6 +143,24 @@ int convrot_gemm_dequant(const int8_t *xq, const float *x_scale,
                          const void *bias_bf16, void *y_bf16,
                          int64_t M, int64_t N, int64_t K, void *stream);
 
+/* ---------------------------------------------------------------- measurement aid
+ * Not a step of the layer and defined by no page: it exists so that a
+ * benchmark can state the rate the matrix cores sustain on this machine,
+ * under its power limit, for given operand bytes.
+ *
+ * Runs `blocks` workgroups of four waves (one per SIMD).  Every lane loads
+ * four 16-byte fragments from a and four from b (a_bytes / 16 and
+ * b_bytes / 16 fragments are cycled through), then issues iters x 16
+ * independent v_mfma_i32_32x32x32_i8 from registers, and writes one int32
+ * checksum to out[blocks * 256].  Integer ops per call:
+ * blocks * 4 * iters * 16 * 65536.  a, b and out are 16-byte aligned device
+ * buffers owned by the caller; asynchronous on `stream`.
+ * Errors: NULL buffer, buffers under 16 bytes, blocks outside [1, 2^20] or
+ * iters < 1 -> CONVROT_EINVAL; misalignment -> CONVROT_EALIGN; launch error
+ * -> CONVROT_EHIP. */
+int convrot_probe_mfma_i8(const int8_t *a, int64_t a_bytes, const int8_t *b, int64_t b_bytes,
+                          int blocks, int iters, int32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -138,3 +138,14 @@ def test_binding_refuses_cpu_tensors(binding):
     import torch
     with pytest.raises(ValueError):
         binding.convrot_rotate_quant(torch.zeros((2, 128), dtype=torch.bfloat16), 128)
+
+
+def test_mfma_probe_argument_errors(lib):
+    f = lib.convrot_probe_mfma_i8
+    assert f(A, 4096, A, 4096, 0, 10, A, None) == EINVAL          # no blocks
+    assert f(A, 4096, A, 4096, 4, 0, A, None) == EINVAL           # no iterations
+    assert f(A, 8, A, 4096, 4, 10, A, None) == EINVAL             # operand under 16 bytes
+    assert f(None, 4096, A, 4096, 4, 10, A, None) == EINVAL
+    assert f(A + 4, 4096, A, 4096, 4, 10, A, None) == EALIGN
+    assert f(A, 4096, A, 4096, 4, 10, A + 8, None) == EALIGN
+    assert b"aligned" in lib.convrot_last_error()

@@ -34,6 +34,7 @@ SIGNATURES = {
     "convrot_rotate_quant": ([_P, _I64, _I64, _I, _P, _P, _P], _I),
     "convrot_gemm_i32": ([_P, _P, _I64, _I64, _I64, _P, _P], _I),
     "convrot_gemm_dequant": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _I),
+    "convrot_probe_mfma_i8": ([_P, _I64, _P, _I64, _I, _I, _P, _P], _I),
 }
 
 
@@ -168,6 +169,21 @@ def convrot_gemm_dequant(xq, x_scale, wq, w_scale, bias=None, out=None) -> torch
     _call("convrot_gemm_dequant", _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias),
           _ptr(y), M, N, K, _stream(xq))
     return y
+
+
+def convrot_probe_mfma_i8(a, b, blocks, iters, out=None) -> torch.Tensor:
+    """Measurement aid: register-only int8 MFMA loop on fragments of the int8
+    tensors a and b (see include/convrot.h); returns the int32 checksums
+    [blocks * 256].  Integer ops: blocks * 4 * iters * 16 * 65536."""
+    _need(a, torch.int8, "a", None)
+    _need(b, torch.int8, "b", None)
+    o = torch.empty(blocks * 256, dtype=torch.int32, device=a.device) if out is None else out
+    _need(o, torch.int32, "out", 1)
+    if o.numel() < blocks * 256:
+        raise ValueError("convrot_probe_mfma_i8: out needs blocks * 256 elements")
+    _call("convrot_probe_mfma_i8", _ptr(a), a.numel(), _ptr(b), b.numel(), blocks, iters, _ptr(o),
+          _stream(a))
+    return o
 
 
 def convrot_linear(x, wq, w_scale, group, bias=None, out=None, workspace=None) -> torch.Tensor:

@@ -184,4 +184,18 @@ int convrot_linear(const void* x_bf16, int64_t M, int64_t K, const int8_t* wq, c
   return ok();
 }
 
+int convrot_probe_mfma_i8(const int8_t* a, int64_t a_bytes, const int8_t* b, int64_t b_bytes,
+                          int blocks, int iters, int32_t* out, void* stream) {
+  const char* who = "convrot_probe_mfma_i8";
+  if (!a || !b || !out) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
+  if (a_bytes < 16 || b_bytes < 16 || blocks < 1 || blocks > (1 << 20) || iters < 1)
+    return fail(CONVROT_EINVAL, "%s: operand buffers need 16+ bytes, blocks in [1, 2^20], iters >= 1",
+                who);
+  if (!aligned16(a) || !aligned16(b) || !aligned16(out))
+    return fail(CONVROT_EALIGN, "%s: a, b and out must be 16-byte aligned", who);
+  return hip_status(convrot::launch_mfma_probe(a, a_bytes, b, b_bytes, blocks, iters, out,
+                                               static_cast<hipStream_t>(stream)),
+                    who);
+}
+
 }  // extern "C"

@@ -1,5 +1,6 @@
 // convrot_internal.hpp -- shared declarations of the HIP library (not part of
-// the C ABI).  Kernels live in rotate_quant.hip and gemm_i8.hip; argument
+// the C ABI).  Kernels live in rotate_quant.hip and gemm_i8.hip (and a
+// measurement loop in mfma_probe.hip); argument
 // checking and dispatch live in convrot_api.hip.
 #pragma once
 
@@ -38,5 +39,13 @@ hipError_t launch_gemm_dequant(const int8_t* xq, const float* x_scale, const int
 // Same main loop with the raw int32 products stored.
 hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// ---------------------------------------------------------------- measurement aid
+
+// Register-only MFMA loop (mfma_probe.hip): `blocks` workgroups of 256
+// threads, `iters` x 16 v_mfma_i32_32x32x32_i8 per wave on 16-byte fragments
+// taken from a and b; one int32 per thread written to out.
+hipError_t launch_mfma_probe(const int8_t* a, int64_t a_bytes, const int8_t* b, int64_t b_bytes,
+                             int blocks, int iters, int32_t* out, hipStream_t stream);
 
 }  // namespace convrot
