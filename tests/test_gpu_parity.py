@@ -44,9 +44,13 @@ def rand_bf16(M, K, seed, outliers=4, factor=20.0):
 
 # ---------------------------------------------------------------- rotate + quant
 
+# Batches of up to 2^21 elements take the row kernel (a row spread over 256
+# lanes), larger ones with K <= 32768 the block kernel (one lane per 128
+# elements, several rows per workgroup), K > 32768 the row kernel in two passes.
 ROTQ_CASES = [
     (5, 128, 128), (131, 512, 128), (300, 3072, 128), (77, 3072, 256), (40, 4096, 128),
     (33, 12288, 128), (20, 12288, 256), (9, 16384, 128), (7, 24576, 256), (3, 131072, 128),
+    (701, 3072, 128), (523, 4096, 256), (171, 12288, 128), (129, 16384, 256), (67, 32768, 128),
 ]
 
 
@@ -263,7 +267,8 @@ def test_every_gemm_tile_is_bit_exact(B, tile, M, N, K, monkeypatch):
     assert np.all(same_bf16(bits_of(y), oracle.epilogue(acc_ref, s_x, s_w, bias)))
 
 
-def test_rotate_quant_exact_ties(B):
+@pytest.mark.parametrize("reps", [1, 700])       # row kernel; block kernel (M*K > 2^21)
+def test_rotate_quant_exact_ties(B, reps):
     # g = 256 rotates exactly (1/sqrt(256) = 1/16): with x = H u the rotated
     # row is 16 u, so with max |u| = 127 the quotient v/s is u itself, and
     # half-integer entries of u land exactly on rounding ties of the code
@@ -278,7 +283,7 @@ def test_rotate_quant_exact_ties(B):
         u = np.zeros(g)
         u[0], u[7], u[9] = 127.0, half, 0.5
         rows.append(H @ u)
-    xf = np.tile(np.array(rows), (1, 2))
+    xf = np.tile(np.array(rows), (reps, 2))
     x = synth.to_bf16_bits(xf)
     assert np.array_equal(oracle.bf16_bits_to_f32(x), xf.astype(np.float32))
     q, s = B.convrot_rotate_quant(to_dev_bf16(x, DEV), g)
