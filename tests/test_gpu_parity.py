@@ -247,7 +247,7 @@ def test_empty_batch_is_a_no_op(B):
     assert y.shape == (0, 8)
 
 
-@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny"])
+@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16"])
 @pytest.mark.parametrize("M,N,K", [(300, 1001, 384), (513, 1000, 1024), (1111, 777, 640)])
 def test_every_gemm_tile_is_bit_exact(B, tile, M, N, K, monkeypatch):
     # the tile shape is a performance choice: every one must give the same bytes
