@@ -19,6 +19,10 @@ arrays through ctypes.  The steps and their sources:
   "int8 Compute", opening section.
 * O6 dequantize with act_scale * weight_scale plus bias to bf16 -- page
   "int8 Compute", "What stays on the default path" (BF16 compute).
+* Variants: fp16 in place of bf16 for the activation, the bias and the output
+  (same page and section: the kernels run in BF16 and FP16), and one weight
+  scale per output channel (page "Explanation of INT8 ConvRot", the format
+  table's row-wise scaling).
 
 Two side outputs are computed here in float64 with numpy, not in C: the
 unquantized product ``x . W^T + bias`` (``reference_fp64``) and the NRMSE
@@ -75,9 +79,18 @@ def _load():
         lib.oracle_gemm_i32.argtypes = [P, P, I64, I64, I64, P]
         lib.oracle_epilogue.argtypes = [P, P, F, P, I64, I64, P]
         lib.oracle_linear_rows.argtypes = [P, I64, I64, P, I64, P, F, I64, I, P, P, P, P]
+        lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_f32.restype = F
+        lib.oracle_f32_to_f16.argtypes = [F]
+        lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+        lib.oracle_quant_weight_rows.argtypes = [P, I64, I64, I, P, P, P]
+        lib.oracle_quant_act_ex.argtypes = [P, I, I64, I64, I, P, P, P]
+        lib.oracle_epilogue_ex.argtypes = [P, P, P, I, P, I, I64, I64, P]
+        lib.oracle_linear_rows_ex.argtypes = [P, I, I64, I64, P, I64, P, P, I, I64, I, P, P, P, P]
         for name in ("oracle_hadamard", "oracle_rotate_rows", "oracle_quant_weight",
                      "oracle_quant_act", "oracle_gemm_i32", "oracle_epilogue",
-                     "oracle_linear_rows"):
+                     "oracle_linear_rows", "oracle_quant_weight_rows", "oracle_quant_act_ex",
+                     "oracle_epilogue_ex", "oracle_linear_rows_ex"):
             getattr(lib, name).restype = I
         _lib = lib
     return _lib
@@ -105,6 +118,26 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 def f32_to_bf16_bits(f) -> int:
     """Round one float32 to bf16 (RNE) through the C oracle."""
     return int(_load().oracle_f32_to_bf16(float(np.float32(f))))
+
+
+def f16_bits_to_f32(h) -> np.ndarray:
+    """Widen IEEE binary16 bit patterns (uint16) to float32 through the C oracle."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    f = _load().oracle_f16_to_f32
+    return np.array([f(int(v)) for v in h.ravel()], dtype=np.float32).reshape(h.shape)
+
+
+def f32_to_f16_bits(x) -> np.ndarray:
+    """Round float32 values to IEEE binary16 bits (RNE) through the C oracle."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    f = _load().oracle_f32_to_f16
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint16).reshape(x.shape)
+
+
+def _io(io: str) -> int:
+    if io not in ("bf16", "f16"):
+        raise ValueError(f"io must be 'bf16' or 'f16', got {io!r}")
+    return 1 if io == "f16" else 0
 
 
 def rot_scale(g: int) -> np.float32:
@@ -140,15 +173,27 @@ def quant_weight(w: np.ndarray, g: int, return_rot: bool = False):
     return (wq, np.float32(s[0]), rot) if return_rot else (wq, np.float32(s[0]))
 
 
-def quant_act(x_bits: np.ndarray, g: int, return_rot: bool = False):
-    """O4: bf16 bits [M, K] -> (int8 [M, K], float32 [M][, rotated fp32])."""
+def quant_weight_rows(w: np.ndarray, g: int, return_rot: bool = False):
+    """Row-wise O3: fp32 [N, K] -> (int8 [N, K], float32 scales [N][, rotated fp32])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    wq = np.empty((N, K), dtype=np.int8)
+    s = np.zeros(N, dtype=np.float32)
+    rot = np.empty((N, K), dtype=np.float32) if return_rot else None
+    _check(_load().oracle_quant_weight_rows(_ptr(w), N, K, int(g), _ptr(wq), _ptr(s), _ptr(rot)),
+           "quant_weight_rows")
+    return (wq, s, rot) if return_rot else (wq, s)
+
+
+def quant_act(x_bits: np.ndarray, g: int, return_rot: bool = False, io: str = "bf16"):
+    """O4: bf16 (or fp16, io="f16") bits [M, K] -> (int8 [M, K], float32 [M][, rotated fp32])."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     M, K = x_bits.shape
     q = np.empty((M, K), dtype=np.int8)
     s = np.empty(M, dtype=np.float32)
     rot = np.empty((M, K), dtype=np.float32) if return_rot else None
-    _check(_load().oracle_quant_act(_ptr(x_bits), M, K, int(g), _ptr(q), _ptr(s), _ptr(rot)),
-           "quant_act")
+    _check(_load().oracle_quant_act_ex(_ptr(x_bits), _io(io), M, K, int(g), _ptr(q), _ptr(s),
+                                       _ptr(rot)), "quant_act")
     return (q, s, rot) if return_rot else (q, s)
 
 
@@ -164,25 +209,36 @@ def gemm_i32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return acc
 
 
-def epilogue(acc: np.ndarray, s_x: np.ndarray, s_w, bias_bits=None) -> np.ndarray:
-    """O6: int32 [M, N] -> bf16 bits [M, N]."""
+def epilogue(acc: np.ndarray, s_x: np.ndarray, s_w, bias_bits=None, io: str = "bf16") -> np.ndarray:
+    """O6: int32 [M, N] -> bf16 (or fp16) bits [M, N].
+
+    s_w: one scale (tensorwise) or an array of N (one per output channel)."""
     acc = np.ascontiguousarray(acc, dtype=np.int32)
     s_x = np.ascontiguousarray(s_x, dtype=np.float32)
     M, N = acc.shape
     bias = None if bias_bits is None else np.ascontiguousarray(bias_bits, dtype=np.uint16)
     y = np.empty((M, N), dtype=np.uint16)
-    _check(_load().oracle_epilogue(_ptr(acc), _ptr(s_x), float(np.float32(s_w)), _ptr(bias),
-                                   M, N, _ptr(y)), "epilogue")
+    sw = np.atleast_1d(np.ascontiguousarray(s_w, dtype=np.float32))
+    row = sw.size > 1 or (np.ndim(s_w) == 1 and N == 1)
+    if row and sw.size != N:
+        raise ValueError("epilogue: s_w must hold 1 or N scales")
+    if not row and io == "bf16":
+        _check(_load().oracle_epilogue(_ptr(acc), _ptr(s_x), float(sw[0]), _ptr(bias),
+                                       M, N, _ptr(y)), "epilogue")
+    else:
+        _check(_load().oracle_epilogue_ex(_ptr(acc), _ptr(s_x), _ptr(sw), int(row), _ptr(bias),
+                                          _io(io), M, N, _ptr(y)), "epilogue")
     return y
 
 
-def linear(x_bits, wq, s_w, g, bias_bits=None):
+def linear(x_bits, wq, s_w, g, bias_bits=None, io: str = "bf16"):
     """The whole layer on every token: O4 -> O5 -> O6.
 
-    Returns (y bf16 bits [M, N], q_x int8 [M, K], s_x float32 [M])."""
-    q, s = quant_act(x_bits, g)
+    Returns (y bits [M, N], q_x int8 [M, K], s_x float32 [M]); x, bias and y
+    are bf16 bits, or fp16 bits with io="f16"; s_w has 1 or N scales."""
+    q, s = quant_act(x_bits, g, io=io)
     acc = gemm_i32(q, wq)
-    return epilogue(acc, s, s_w, bias_bits), q, s
+    return epilogue(acc, s, s_w, bias_bits, io=io), q, s
 
 
 def linear_rows(x_bits, rows, wq, s_w, g, bias_bits=None):
@@ -202,6 +258,26 @@ def linear_rows(x_bits, rows, wq, s_w, g, bias_bits=None):
     _check(_load().oracle_linear_rows(_ptr(x_bits), M, K, _ptr(rows), R, _ptr(wq),
                                       float(np.float32(s_w)), N, int(g), _ptr(bias),
                                       _ptr(y), _ptr(q), _ptr(s)), "linear_rows")
+    return y, q, s
+
+
+def linear_rows_ex(x_bits, rows, wq, s_w, g, bias_bits=None, io: str = "bf16"):
+    """linear_rows with the variants (io = "bf16" | "f16"; s_w: 1 or N scales)."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    wq = np.ascontiguousarray(wq, dtype=np.int8)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    M, K = x_bits.shape
+    N = wq.shape[0]
+    R = rows.shape[0]
+    sw = np.atleast_1d(np.ascontiguousarray(s_w, dtype=np.float32))
+    row = sw.size > 1 or (np.ndim(s_w) == 1 and N == 1)
+    bias = None if bias_bits is None else np.ascontiguousarray(bias_bits, dtype=np.uint16)
+    y = np.empty((R, N), dtype=np.uint16)
+    q = np.empty((R, K), dtype=np.int8)
+    s = np.empty(R, dtype=np.float32)
+    _check(_load().oracle_linear_rows_ex(_ptr(x_bits), _io(io), M, K, _ptr(rows), R, _ptr(wq),
+                                         _ptr(sw), int(row), N, int(g), _ptr(bias), _ptr(y),
+                                         _ptr(q), _ptr(s)), "linear_rows_ex")
     return y, q, s
 
 

@@ -48,6 +48,59 @@ uint16_t oracle_f32_to_bf16(float f)
     return (uint16_t)(u >> 16);
 }
 
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Widening decodes the three classes (zero/subnormal, normal, inf/NaN)
+ * exactly. */
+float oracle_f16_to_f32(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int e = (h >> 10) & 0x1f;
+    const int m = h & 0x3ff;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)m, -24);                 /* m * 2^-24: zero or subnormal */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(1024 + m), e - 25);     /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* Narrowing to binary16, round to nearest, ties to even.  Magnitudes of at
+ * least 65520 (halfway between the largest finite 65504 and 2^16) become
+ * infinity; below 2^-14 the spacing is the subnormal quantum 2^-24. */
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    u &= 0x7fffffffu;
+    if (u > 0x7f800000u) return (uint16_t)(sign | 0x7e00u);      /* NaN */
+    if (u >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u);     /* >= 65520: inf */
+    if (u < 0x38800000u) {                                        /* below 2^-14 */
+        float a;
+        memcpy(&a, &u, sizeof a);
+        /* a * 2^24 is exact; nearbyintf rounds half to even */
+        return (uint16_t)(sign | (uint16_t)nearbyintf(a * 16777216.0f));
+    }
+    /* normal: rebias the exponent, keep 10 of the 23 fraction bits, round on
+     * the 13 dropped ones (a carry out of the fraction bumps the exponent) */
+    uint32_t h = ((((u >> 23) & 0xffu) - 127u + 15u) << 10) | ((u >> 13) & 0x3ffu);
+    const uint32_t rem = u & 0x1fffu;
+    if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1u;
+    return (uint16_t)(sign | h);
+}
+
+static float io_to_f32(uint16_t b, int io_f16)
+{
+    return io_f16 ? oracle_f16_to_f32(b) : oracle_bf16_to_f32(b);
+}
+
+static uint16_t f32_to_io(float f, int io_f16)
+{
+    return io_f16 ? oracle_f32_to_f16(f) : oracle_f32_to_bf16(f);
+}
+
 float oracle_rot_scale(int g)
 {
     return (float)(1.0 / sqrt((double)g));
@@ -131,11 +184,38 @@ int oracle_quant_weight(const float *w, int64_t N, int64_t K, int g,
     return 0;
 }
 
-/* O4 for one token row: widen bf16 -> fp32, rotate, absmax, scale, codes. */
-static void quant_act_row(const uint16_t *xrow, int64_t K, int g, float *rot,
+/* Row-wise variant of O3: the same rotation, one absmax and one scale per
+ * output channel (row n), as for a token in O4. */
+int oracle_quant_weight_rows(const float *w, int64_t N, int64_t K, int g,
+                             int8_t *wq, float *s_w, float *w_rot)
+{
+    if (!is_pow2(g) || N < 1 || K < 1 || (K % g) != 0 || w == NULL || wq == NULL || s_w == NULL)
+        return -1;
+    float *rot = (float *)malloc((size_t)K * sizeof(float));
+    if (rot == NULL) return -3;
+    for (int64_t n = 0; n < N; ++n) {
+        memcpy(rot, w + n * K, (size_t)K * sizeof(float));
+        oracle_rotate_rows(rot, 1, K, g);
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(rot[k]);
+            if (a > amax) amax = a;
+        }
+        float s = amax / 127.0f;
+        for (int64_t k = 0; k < K; ++k) wq[n * K + k] = quant_code(rot[k], s);
+        s_w[n] = s;
+        if (w_rot) memcpy(w_rot + n * K, rot, (size_t)K * sizeof(float));
+    }
+    free(rot);
+    return 0;
+}
+
+/* O4 for one token row: widen bf16 (or fp16) -> fp32, rotate, absmax,
+ * scale, codes. */
+static void quant_act_row(const uint16_t *xrow, int io_f16, int64_t K, int g, float *rot,
                           int8_t *qrow, float *srow)
 {
-    for (int64_t k = 0; k < K; ++k) rot[k] = oracle_bf16_to_f32(xrow[k]);
+    for (int64_t k = 0; k < K; ++k) rot[k] = io_to_f32(xrow[k], io_f16);
     oracle_rotate_rows(rot, 1, K, g);
     float amax = 0.0f;
     for (int64_t k = 0; k < K; ++k) {
@@ -150,12 +230,18 @@ static void quant_act_row(const uint16_t *xrow, int64_t K, int g, float *rot,
 int oracle_quant_act(const uint16_t *x, int64_t M, int64_t K, int g,
                      int8_t *q, float *s, float *x_rot)
 {
+    return oracle_quant_act_ex(x, 0, M, K, g, q, s, x_rot);
+}
+
+int oracle_quant_act_ex(const uint16_t *x, int io_f16, int64_t M, int64_t K, int g,
+                        int8_t *q, float *s, float *x_rot)
+{
     if (!is_pow2(g) || M < 0 || K < 1 || (K % g) != 0 || (M > 0 && (x == NULL || q == NULL || s == NULL)))
         return -1;
     float *rot = (float *)malloc((size_t)K * sizeof(float));
     if (rot == NULL) return -3;
     for (int64_t m = 0; m < M; ++m) {
-        quant_act_row(x + m * K, K, g, rot, q + m * K, s + m);
+        quant_act_row(x + m * K, io_f16, K, g, rot, q + m * K, s + m);
         if (x_rot) memcpy(x_rot + m * K, rot, (size_t)K * sizeof(float));
     }
     free(rot);
@@ -199,6 +285,25 @@ int oracle_epilogue(const int32_t *acc, const float *s_x, float s_w,
     return 0;
 }
 
+/* O6 with the variants: s_w holds one scale (row_scale = 0) or one per
+ * output channel (row_scale = 1), alpha = s_x[m] * s_w[n or 0] in fp32; the
+ * bias and the output are bf16 (io_f16 = 0) or fp16 (io_f16 = 1) bits. */
+int oracle_epilogue_ex(const int32_t *acc, const float *s_x, const float *s_w, int row_scale,
+                       const uint16_t *bias, int io_f16, int64_t M, int64_t N, uint16_t *y)
+{
+    if (M < 0 || N < 0 || ((M > 0 && N > 0) && (acc == NULL || s_x == NULL || s_w == NULL || y == NULL)))
+        return -1;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            float alpha = s_x[m] * s_w[row_scale ? n : 0];
+            float bn = bias ? io_to_f32(bias[n], io_f16) : 0.0f;
+            float v = fmaf((float)acc[m * N + n], alpha, bn);
+            y[m * N + n] = f32_to_io(v, io_f16);
+        }
+    }
+    return 0;
+}
+
 int oracle_linear_rows(const uint16_t *x, int64_t M, int64_t K,
                        const int64_t *rows, int64_t R,
                        const int8_t *wq, float s_w, int64_t N, int g,
@@ -219,9 +324,39 @@ int oracle_linear_rows(const uint16_t *x, int64_t M, int64_t K,
     int rc = 0;
     for (int64_t r = 0; r < R; ++r) {
         float s;
-        quant_act_row(x + rows[r] * K, K, g, rot, q, &s);
+        quant_act_row(x + rows[r] * K, 0, K, g, rot, q, &s);
         if (oracle_gemm_i32(q, wq, 1, N, K, acc) != 0) rc = -2;
         oracle_epilogue(acc, &s, s_w, bias, 1, N, y + r * N);
+        if (q_rows) memcpy(q_rows + r * K, q, (size_t)K);
+        if (s_rows) s_rows[r] = s;
+    }
+    free(rot); free(q); free(acc);
+    return rc;
+}
+
+int oracle_linear_rows_ex(const uint16_t *x, int io_f16, int64_t M, int64_t K,
+                          const int64_t *rows, int64_t R,
+                          const int8_t *wq, const float *s_w, int row_scale, int64_t N, int g,
+                          const uint16_t *bias, uint16_t *y,
+                          int8_t *q_rows, float *s_rows)
+{
+    if (!is_pow2(g) || M < 1 || K < 1 || N < 1 || R < 0 || (K % g) != 0 ||
+        x == NULL || wq == NULL || s_w == NULL || y == NULL || (R > 0 && rows == NULL))
+        return -1;
+    for (int64_t r = 0; r < R; ++r)
+        if (rows[r] < 0 || rows[r] >= M) return -1;
+
+    float *rot = (float *)malloc((size_t)K * sizeof(float));
+    int8_t *q = (int8_t *)malloc((size_t)K);
+    int32_t *acc = (int32_t *)malloc((size_t)N * sizeof(int32_t));
+    if (!rot || !q || !acc) { free(rot); free(q); free(acc); return -3; }
+
+    int rc = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        float s;
+        quant_act_row(x + rows[r] * K, io_f16, K, g, rot, q, &s);
+        if (oracle_gemm_i32(q, wq, 1, N, K, acc) != 0) rc = -2;
+        oracle_epilogue_ex(acc, &s, s_w, row_scale, bias, io_f16, 1, N, y + r * N);
         if (q_rows) memcpy(q_rows + r * K, q, (size_t)K);
         if (s_rows) s_rows[r] = s;
     }

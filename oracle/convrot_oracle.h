@@ -25,6 +25,9 @@
  *   scales: s = absmax / 127 (fp32, IEEE division); codes q = clamp(rne(v/s),
  *        -127, 127); an all-zero row/tensor gives s = 0 and codes 0.
  *   epilogue: y = bf16_rne(fmaf((float)acc, s_x[m]*s_w, bias[n])).
+ *   variants: fp16 in place of bf16 for x, bias and y (IEEE binary16, RNE,
+ *        overflow to infinity); one weight scale per output channel, computed
+ *        like a token's (alpha = s_x[m] * s_w[n]).
  *
  * All arrays are row-major and contiguous.  bf16 values travel as their raw
  * uint16 bit patterns.  Functions return 0 on success and a negative value on
@@ -43,6 +46,11 @@ extern "C" {
 float    oracle_bf16_to_f32(uint16_t b);
 uint16_t oracle_f32_to_bf16(float f);
 
+/* float <-> IEEE binary16 bit conversions (widening exact; narrowing RNE,
+ * overflow to infinity, gradual underflow). */
+float    oracle_f16_to_f32(uint16_t h);
+uint16_t oracle_f32_to_f16(float f);
+
 /* c_g: the float nearest to 1/sqrt(g). */
 float oracle_rot_scale(int g);
 
@@ -59,10 +67,20 @@ int oracle_rotate_rows(float *v, int64_t rows, int64_t K, int g);
 int oracle_quant_weight(const float *w, int64_t N, int64_t K, int g,
                         int8_t *wq, float *s_w, float *w_rot);
 
+/* Row-wise variant of O3 (page "Explanation of INT8 ConvRot", format table:
+ * row-wise scaling): s_w: fp32 [N], one scale per output channel. */
+int oracle_quant_weight_rows(const float *w, int64_t N, int64_t K, int g,
+                             int8_t *wq, float *s_w, float *w_rot);
+
 /* O4: per-token activation quantization.  x: bf16 bits [M, K].
  * q: int8 [M, K]; s: fp32 [M].  x_rot (nullable): fp32 [M, K]. */
 int oracle_quant_act(const uint16_t *x, int64_t M, int64_t K, int g,
                      int8_t *q, float *s, float *x_rot);
+
+/* O4 with fp16 input bits when io_f16 != 0 (page "int8 Compute", "What
+ * stays on the default path": the kernels run in BF16 and FP16). */
+int oracle_quant_act_ex(const uint16_t *x, int io_f16, int64_t M, int64_t K, int g,
+                        int8_t *q, float *s, float *x_rot);
 
 /* O5: acc[m][n] = sum_k a[m][k] * b[n][k], accumulated in int64.
  * Returns -2 if a result does not fit int32. */
@@ -74,6 +92,12 @@ int oracle_gemm_i32(const int8_t *a, const int8_t *b, int64_t M, int64_t N,
 int oracle_epilogue(const int32_t *acc, const float *s_x, float s_w,
                     const uint16_t *bias, int64_t M, int64_t N, uint16_t *y);
 
+/* O6 variants: y[m][n] = rnd(fmaf((float)acc, s_x[m] * s_w[row_scale ? n : 0],
+ * bias[n])), rnd = bf16 (io_f16 = 0) or fp16 (io_f16 = 1) RNE; bias in the
+ * same format, or NULL. */
+int oracle_epilogue_ex(const int32_t *acc, const float *s_x, const float *s_w, int row_scale,
+                       const uint16_t *bias, int io_f16, int64_t M, int64_t N, uint16_t *y);
+
 /* O4 -> O5 -> O6 for the rows of x listed in rows[0..R) (R rows, each index
  * in [0, M)).  Output y: bf16 bits [R, N]; q_rows: int8 [R, K] and s_rows:
  * fp32 [R] (both nullable) receive the rows' codes and scales.  wq/s_w come
@@ -84,6 +108,14 @@ int oracle_linear_rows(const uint16_t *x, int64_t M, int64_t K,
                        const int8_t *wq, float s_w, int64_t N, int g,
                        const uint16_t *bias, uint16_t *y,
                        int8_t *q_rows, float *s_rows);
+
+/* oracle_linear_rows with the variants: x, bias and y in bf16 or fp16 bits
+ * (io_f16), s_w with one or N entries (row_scale). */
+int oracle_linear_rows_ex(const uint16_t *x, int io_f16, int64_t M, int64_t K,
+                          const int64_t *rows, int64_t R,
+                          const int8_t *wq, const float *s_w, int row_scale, int64_t N, int g,
+                          const uint16_t *bias, uint16_t *y,
+                          int8_t *q_rows, float *s_rows);
 
 #ifdef __cplusplus
 }

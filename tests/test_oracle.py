@@ -425,3 +425,174 @@ def test_checker_rejects_zero_output_and_flipped_codes(golden_dir):
     q_bad[0:16, 0:64] = -q_bad[0:16, 0:64]
     y_bad = oracle.epilogue(oracle.gemm_i32(q_bad, wq), s, s_w, L.bias_bits)
     assert oracle.nrmse(oracle.bf16_bits_to_f32(y_bad), yf) > 1e-2
+
+
+# ---------------------------------------------------------------- variants: fp16 I/O, row-wise weight scales
+
+def rn_f16(q: Fraction) -> Fraction:
+    """Exact round-to-nearest-even of a rational to binary16 (finite range):
+    spacing 2^(e-10) for |q| in [2^e, 2^(e+1)), e >= -14, and 2^-24 below 2^-14."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (max(e, -14) - 10)
+    m = a / ulp
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * ulp
+
+
+def f16_value(bits: int) -> Fraction:
+    """The exact value of a finite binary16 bit pattern, from the format."""
+    sign = -1 if bits & 0x8000 else 1
+    e, f = (bits >> 10) & 0x1F, bits & 0x3FF
+    assert e != 31
+    if e == 0:
+        return sign * Fraction(f, 2 ** 24)
+    return sign * Fraction(1024 + f, 1024) * Fraction(2) ** (e - 15)
+
+
+def test_f16_rounding_table(golden_dir):
+    rows = []
+    for line in open(os.path.join(golden_dir, "f16_rne.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            v, b = line.split()[:2]
+            rows.append((float.fromhex(v), int(b, 16)))
+    assert len(rows) >= 20
+    vals = np.array([v for v, _ in rows], dtype=np.float32)
+    assert all(float(np.float32(v)) == v for v, _ in rows)      # every case is a binary32 value
+    got = oracle.f32_to_f16_bits(vals)
+    assert [int(b) for b in got] == [b for _, b in rows]
+
+
+def test_f16_rounding_against_exact_rationals():
+    # random binary32 values over the whole finite binary16 range, subnormals included
+    r = np.random.default_rng(16)
+    v = (r.standard_normal(4000) * np.exp2(r.integers(-26, 16, 4000))).astype(np.float32)
+    v = v[np.abs(v) < 65504]
+    got = oracle.f32_to_f16_bits(v)
+    for x, b in zip(v, got):
+        assert f16_value(int(b)) == rn_f16(Fraction(float(x))), (float(x), hex(int(b)))
+
+
+def test_f16_conversions_match_numpy():
+    # an independent implementation of the same IEEE conversions
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    wide = oracle.f16_bits_to_f32(allbits)
+    ref = allbits.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(wide), nan)
+    assert np.array_equal(wide[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    r = np.random.default_rng(17)
+    v = (r.standard_normal(20000) * np.exp2(r.integers(-30, 20, 20000))).astype(np.float32)
+    with np.errstate(over="ignore"):
+        assert np.array_equal(oracle.f32_to_f16_bits(v), v.astype(np.float16).view(np.uint16))
+
+
+def test_rowwise_weight_one_row_is_tensorwise():
+    w = np.random.default_rng(3).standard_normal((1, 512)).astype(np.float32)
+    q_t, s_t = oracle.quant_weight(w, 128)
+    q_r, s_r = oracle.quant_weight_rows(w, 128)
+    assert np.array_equal(q_t, q_r) and s_r.shape == (1,) and s_r[0] == s_t
+
+
+def test_rowwise_weight_rows_are_independent():
+    r = np.random.default_rng(4)
+    w = (r.standard_normal((6, 256)) * 0.02).astype(np.float32)
+    w[2] = 0.0                                             # a zero channel
+    q, s = oracle.quant_weight_rows(w, 128)
+    for n in range(6):
+        qn, sn = oracle.quant_weight_rows(w[n:n + 1], 128)
+        assert np.array_equal(qn[0], q[n]) and sn[0] == s[n]
+    assert s[2] == 0 and not q[2].any()
+    # a power-of-two scale of one row scales its scale and keeps its codes
+    w2 = w.copy()
+    w2[4] *= np.float32(8.0)
+    q2, s2 = oracle.quant_weight_rows(w2, 128)
+    assert np.array_equal(q2, q) and s2[4] == 8 * s[4] and np.array_equal(np.delete(s2, 4), np.delete(s, 4))
+    # every nonzero channel uses the full code range
+    assert np.abs(q).max() <= 127
+    for n in (0, 1, 3, 4, 5):
+        assert np.abs(q[n].astype(int)).max() == 127
+
+
+def test_rowwise_weight_identity_rotation_is_textbook_rtn():
+    w = np.array([[1.0, -2.0, 0.5, 4.0], [3.0, 0.25, -6.0, 1.5]], dtype=np.float32)
+    q, s = oracle.quant_weight_rows(w, 1)
+    # row 0: s = 4/127, codes 127/4 * [1, -2, 0.5, 4] = [31.75, -63.5, 15.875, 127]
+    # row 1: s = 6/127, codes 127/6 * [3, 0.25, -6, 1.5] = [63.5, 5.29, -127, 31.75]
+    assert q.tolist() == [[32, -64, 16, 127], [64, 5, -127, 32]]
+    assert s[0] == np.float32(4.0) / np.float32(127.0) and s[1] == np.float32(6.0) / np.float32(127.0)
+
+
+def test_epilogue_variants_against_exact_rationals():
+    r = np.random.default_rng(18)
+    M, N = 5, 9
+    acc = r.integers(-2 ** 22, 2 ** 22, (M, N)).astype(np.int32)
+    s_x = (r.random(M) * 1e-3 + 1e-6).astype(np.float32)
+    s_w = (r.random(N) * 1e-4 + 1e-7).astype(np.float32)
+    bias_f16 = oracle.f32_to_f16_bits((r.standard_normal(N) * 0.5).astype(np.float32))
+    bias_bf16 = synth.to_bf16_bits(r.standard_normal(N) * 0.5)
+    for io, bias, widen, rnd in (("f16", bias_f16, lambda b: f16_value(int(b)), rn_f16),
+                                 ("bf16", bias_bf16, lambda b: Fraction(float(oracle.bf16_bits_to_f32(np.array([b], dtype=np.uint16))[0])),
+                                  None)):
+        for row in (True, False):
+            sw = s_w if row else s_w[:1]
+            y = oracle.epilogue(acc, s_x, sw if row else sw[0], bias, io=io)
+            for m in range(M):
+                for n in range(N):
+                    alpha = rn_float32(Fraction(float(s_x[m])) * Fraction(float(sw[n if row else 0])))
+                    v = rn_float32(Fraction(int(acc[m, n])) * alpha + widen(bias[n]))
+                    if io == "f16":
+                        assert f16_value(int(y[m, n])) == rnd(v)
+                    else:
+                        assert y[m, n] == oracle.f32_to_bf16_bits(np.float32(float(v)))
+
+
+def test_quant_act_f16_input():
+    r = np.random.default_rng(19)
+    # values exact in both formats give the bf16 path's codes
+    x = synth.to_bf16_bits(r.standard_normal((3, 256)))
+    xf = oracle.bf16_bits_to_f32(x)
+    ok = np.all((np.abs(xf) < 60000) & ((np.abs(xf) >= 2 ** -14) | (xf == 0)), axis=1)
+    assert ok.all()
+    x16 = oracle.f32_to_f16_bits(xf)
+    assert np.array_equal(oracle.f16_bits_to_f32(x16), xf)
+    q_b, s_b = oracle.quant_act(x, 128)
+    q_h, s_h = oracle.quant_act(x16, 128, io="f16")
+    assert np.array_equal(q_b, q_h) and np.array_equal(s_b, s_h)
+    # fp16 values with more fraction bits than bf16 holds, identity rotation:
+    # textbook round-to-nearest of the widened values
+    v = np.array([[1.0009766, -0.33325195, 2.5, -7.9960938]], dtype=np.float32)
+    v16 = oracle.f32_to_f16_bits(v)
+    vw = oracle.f16_bits_to_f32(v16).astype(np.float64)
+    q, s = oracle.quant_act(v16, 1, io="f16")
+    sx = np.float32(np.float32(np.abs(vw).max()) / np.float32(127.0))
+    assert s[0] == sx
+    assert q[0].tolist() == [int(np.rint(np.float32(t) / sx)) for t in vw[0].astype(np.float32)]
+
+
+def test_linear_variants_rows_match_full_layer():
+    r = np.random.default_rng(20)
+    M, K, N = 7, 256, 12
+    x = oracle.f32_to_f16_bits(r.standard_t(4, (M, K)).astype(np.float32))
+    w = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bias = oracle.f32_to_f16_bits((r.standard_normal(N) * 0.01).astype(np.float32))
+    wq, s_w = oracle.quant_weight_rows(w, 128)
+    y, q, s = oracle.linear(x, wq, s_w, 128, bias, io="f16")
+    rows = np.array([6, 0, 3])
+    yr, qr, sr = oracle.linear_rows_ex(x, rows, wq, s_w, 128, bias, io="f16")
+    assert np.array_equal(yr, y[rows]) and np.array_equal(qr, q[rows]) and np.array_equal(sr, s[rows])
+    # the variant layer still approximates the unquantized product
+    ref = oracle.f16_bits_to_f32(x).astype(np.float64) @ w.astype(np.float64).T \
+        + oracle.f16_bits_to_f32(bias).astype(np.float64)
+    assert oracle.nrmse(oracle.f16_bits_to_f32(y), ref) < 0.05
