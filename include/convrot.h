@@ -69,7 +69,11 @@ enum convrot_status {
     CONVROT_EHIP = -5           /* a HIP launch or query failed               */
 };
 
-enum convrot_dtype { CONVROT_F32 = 0, CONVROT_BF16 = 1 };
+enum convrot_dtype { CONVROT_F32 = 0, CONVROT_BF16 = 1, CONVROT_F16 = 2 };
+
+/* Weight scale granularity of the _ex entry points: one scale for the whole
+ * weight (int8_tensorwise) or one per output channel (row n of W). */
+enum convrot_scale_mode { CONVROT_SCALE_TENSOR = 0, CONVROT_SCALE_ROW = 1 };
 
 /* CONVROT_ABI_VERSION of the built library. */
 int convrot_abi_version(void);
@@ -142,6 +146,47 @@ int convrot_gemm_dequant(const int8_t *xq, const float *x_scale,
                          const int8_t *wq, const float *w_scale,
                          const void *bias_bf16, void *y_bf16,
                          int64_t M, int64_t N, int64_t K, void *stream);
+
+/* ---------------------------------------------------------------- variants
+ * The layer in FP16 (page "int8 Compute", "What stays on the default path":
+ * the kernels run in BF16 and FP16) and with one weight scale per output
+ * channel (page "Explanation of INT8 ConvRot", format table: row-wise
+ * scaling).  Same kernels and the same definitions as above, except:
+ *   - io_dtype / x_dtype CONVROT_F16: the activation, the bias and the output
+ *     are IEEE binary16 bit patterns; fp16 -> fp32 widening is exact and the
+ *     output is fp16_rne(fmaf(...)), with overflow to infinity;
+ *   - scale_mode CONVROT_SCALE_ROW: s_w holds N scales, each row of W R is
+ *     quantized like a token (s_w[n] = max_k |(W R)[n][k]| / 127), and the
+ *     epilogue uses alpha = s_x[m] * s_w[n] (one fp32 product).
+ * io_dtype / x_dtype: CONVROT_BF16 or CONVROT_F16, else
+ * CONVROT_EUNSUPPORTED; scale_mode: CONVROT_SCALE_TENSOR or CONVROT_SCALE_ROW,
+ * else CONVROT_EUNSUPPORTED.  Every other rule is that of the entry point
+ * without _ex. */
+
+/* convrot_prepare_weight with w_dtype CONVROT_F32, CONVROT_BF16 or
+ * CONVROT_F16 and a scale mode; w_scale_out has 1 (tensor) or N (row)
+ * floats.  The workspace is that of convrot_prepare_weight (row mode leaves
+ * it untouched). */
+int convrot_prepare_weight_ex(const void *w, int w_dtype, int64_t N, int64_t K, int group,
+                              int scale_mode, int8_t *wq_out, float *w_scale_out,
+                              void *workspace, size_t ws_bytes, void *stream);
+
+/* convrot_rotate_quant for a bf16 or fp16 activation. */
+int convrot_rotate_quant_ex(const void *x, int x_dtype, int64_t M, int64_t K, int group,
+                            int8_t *xq, float *x_scale, void *stream);
+
+/* convrot_gemm_dequant with a scale mode (w_scale: 1 or N floats) and bf16
+ * or fp16 bias (nullable) and output. */
+int convrot_gemm_dequant_ex(const int8_t *xq, const float *x_scale, const int8_t *wq,
+                            const float *w_scale, int scale_mode, const void *bias, void *y,
+                            int io_dtype, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* convrot_linear with bf16 or fp16 activation, bias and output, and a scale
+ * mode.  Same workspace (convrot_linear_workspace) and slicing. */
+int convrot_linear_ex(const void *x, int io_dtype, int64_t M, int64_t K, const int8_t *wq,
+                      const float *w_scale, int scale_mode, int64_t N, int group,
+                      const void *bias, void *y, void *workspace, size_t ws_bytes,
+                      void *stream);
 
 /* ---------------------------------------------------------------- measurement aid
  * Not a step of the layer and defined by no page: it exists so that a

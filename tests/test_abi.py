@@ -149,3 +149,21 @@ def test_mfma_probe_argument_errors(lib):
     assert f(A + 4, 4096, A, 4096, 4, 10, A, None) == EALIGN
     assert f(A, 4096, A, 4096, 4, 10, A + 8, None) == EALIGN
     assert b"aligned" in lib.convrot_last_error()
+
+
+def test_variant_argument_errors(lib):
+    F16 = 2
+    # unknown io dtype / scale mode
+    assert lib.convrot_rotate_quant_ex(A, 7, 4, 512, 128, A, A, None) == EUNSUPPORTED
+    assert lib.convrot_gemm_dequant_ex(A, A, A, A, 2, None, A, 1, 4, 4, 256, None) == EUNSUPPORTED
+    assert lib.convrot_gemm_dequant_ex(A, A, A, A, 0, None, A, 0, 4, 4, 256, None) == EUNSUPPORTED
+    assert lib.convrot_linear_ex(A, F16, 64, 512, A, A, 5, 64, 128, None, A, A, 1 << 20, None) == EUNSUPPORTED
+    assert lib.convrot_prepare_weight_ex(A, 0, 64, 512, 128, 3, A, A, A, 256, None) == EUNSUPPORTED
+    # fp16 weights go through the _ex entry point only
+    assert lib.convrot_prepare_weight(A, F16, 64, 512, 128, A, A, A, 256, None) == EUNSUPPORTED
+    assert b"_ex" in lib.convrot_last_error()
+    # the rules of the plain entry points still apply
+    assert lib.convrot_linear_ex(A, F16, 64, 500, A, A, 1, 64, 128, None, A, A, 1 << 20, None) == EINVAL
+    assert lib.convrot_linear_ex(A + 2, F16, 64, 512, A, A, 1, 64, 128, None, A, A, 1 << 20, None) == EALIGN
+    assert lib.convrot_gemm_dequant_ex(A, A, A, A, 1, None, A + 4, F16, 4, 4, 256, None) == EALIGN
+    assert lib.convrot_linear_ex(None, F16, 0, 512, None, None, 1, 64, 128, None, None, None, 0, None) == OK

@@ -18,6 +18,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconvrot.
 
 CONVROT_F32 = 0
 CONVROT_BF16 = 1
+CONVROT_F16 = 2
+CONVROT_SCALE_TENSOR = 0
+CONVROT_SCALE_ROW = 1
 
 STATUS = {0: "CONVROT_OK", -1: "CONVROT_EINVAL", -2: "CONVROT_EUNSUPPORTED",
           -3: "CONVROT_EALIGN", -4: "CONVROT_EWORKSPACE", -5: "CONVROT_EHIP"}
@@ -35,6 +38,10 @@ SIGNATURES = {
     "convrot_gemm_i32": ([_P, _P, _I64, _I64, _I64, _P, _P], _I),
     "convrot_gemm_dequant": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _I),
     "convrot_probe_mfma_i8": ([_P, _I64, _P, _I64, _I, _I, _P, _P], _I),
+    "convrot_prepare_weight_ex": ([_P, _I, _I64, _I64, _I, _I, _P, _P, _P, _SZ, _P], _I),
+    "convrot_rotate_quant_ex": ([_P, _I, _I64, _I64, _I, _P, _P, _P], _I),
+    "convrot_gemm_dequant_ex": ([_P, _P, _P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _P], _I),
+    "convrot_linear_ex": ([_P, _I, _I64, _I64, _P, _P, _I, _I64, _I, _P, _P, _P, _SZ, _P], _I),
 }
 
 
@@ -213,4 +220,113 @@ def convrot_linear(x, wq, w_scale, group, bias=None, out=None, workspace=None) -
         raise ValueError("convrot_linear: output shape mismatch")
     _call("convrot_linear", _ptr(x), M, K, _ptr(wq), _ptr(w_scale), N, group, _ptr(bias), _ptr(y),
           _ptr(workspace), workspace.numel(), _stream(x))
+    return y
+
+
+# ---------------------------------------------------------------- variants (fp16 I/O, row-wise weight scales)
+
+_IO = {torch.bfloat16: CONVROT_BF16, torch.float16: CONVROT_F16}
+
+
+def _io_of(t, name):
+    if t.dtype not in _IO:
+        raise ValueError(f"{name}: expected bfloat16 or float16, got {t.dtype}")
+    return _IO[t.dtype]
+
+
+def convrot_prepare_weight_ex(w: torch.Tensor, group: int, scale_mode: str = "tensor"):
+    """fp32, bf16 or fp16 weight [N, K] -> (int8 codes [N, K], fp32 scales [1] or [N]).
+
+    scale_mode "tensor": one scale; "row": one per output channel."""
+    dt = {torch.float32: CONVROT_F32, torch.bfloat16: CONVROT_BF16, torch.float16: CONVROT_F16}.get(w.dtype)
+    if dt is None:
+        raise ValueError("convrot_prepare_weight_ex: weight must be float32, bfloat16 or float16")
+    if scale_mode not in ("tensor", "row"):
+        raise ValueError("convrot_prepare_weight_ex: scale_mode is 'tensor' or 'row'")
+    _need(w, w.dtype, "w", 2)
+    N, K = w.shape
+    wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
+    s = torch.empty(N if scale_mode == "row" else 1, dtype=torch.float32, device=w.device)
+    ws_bytes = convrot_prepare_weight_workspace(N, K)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=w.device)
+    mode = CONVROT_SCALE_ROW if scale_mode == "row" else CONVROT_SCALE_TENSOR
+    _call("convrot_prepare_weight_ex", _ptr(w), dt, N, K, group, mode, _ptr(wq), _ptr(s), _ptr(ws),
+          ws_bytes, _stream(w))
+    return wq, s
+
+
+def convrot_rotate_quant_ex(x: torch.Tensor, group: int, q=None, s=None):
+    """bf16 or fp16 [M, K] -> (int8 codes [M, K], fp32 scales [M])."""
+    io = _io_of(x, "x")
+    _need(x, x.dtype, "x", 2)
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=x.device) if q is None else q
+    s = torch.empty(M, dtype=torch.float32, device=x.device) if s is None else s
+    _need(q, torch.int8, "q", 2)
+    _need(s, torch.float32, "s", 1)
+    _call("convrot_rotate_quant_ex", _ptr(x), io, M, K, group, _ptr(q), _ptr(s), _stream(x))
+    return q, s
+
+
+def _scale_mode_of(w_scale, N, who):
+    if w_scale.numel() == 1:
+        return CONVROT_SCALE_TENSOR
+    if w_scale.numel() == N:
+        return CONVROT_SCALE_ROW
+    raise ValueError(f"{who}: w_scale must hold 1 or N scales")
+
+
+def convrot_gemm_dequant_ex(xq, x_scale, wq, w_scale, bias=None, out=None,
+                            out_dtype=torch.bfloat16) -> torch.Tensor:
+    """int8 codes and scales -> bf16 or fp16 [M, N]; w_scale holds 1 or N scales,
+    bias (nullable) has the output dtype."""
+    _need(xq, torch.int8, "xq", 2)
+    _need(wq, torch.int8, "wq", 2)
+    _need(x_scale, torch.float32, "x_scale", 1)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or x_scale.numel() != M:
+        raise ValueError("convrot_gemm_dequant_ex: shape mismatch")
+    mode = _scale_mode_of(w_scale, N, "convrot_gemm_dequant_ex")
+    y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    io = _io_of(y, "out")
+    _need(y, y.dtype, "out", 2)
+    if bias is not None:
+        _need(bias, y.dtype, "bias", 1)
+        if bias.numel() != N:
+            raise ValueError("convrot_gemm_dequant_ex: bias must have N elements")
+    if tuple(y.shape) != (M, N):
+        raise ValueError("convrot_gemm_dequant_ex: output shape mismatch")
+    _call("convrot_gemm_dequant_ex", _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), mode, _ptr(bias),
+          _ptr(y), io, M, N, K, _stream(xq))
+    return y
+
+
+def convrot_linear_ex(x, wq, w_scale, group, bias=None, out=None, workspace=None) -> torch.Tensor:
+    """The whole layer in bf16 or fp16 (x, bias and y share x's dtype), with one
+    weight scale or one per output channel (w_scale of 1 or N floats)."""
+    io = _io_of(x, "x")
+    _need(x, x.dtype, "x", 2)
+    _need(wq, torch.int8, "wq", 2)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("convrot_linear_ex: K mismatch")
+    mode = _scale_mode_of(w_scale, N, "convrot_linear_ex")
+    if bias is not None:
+        _need(bias, x.dtype, "bias", 1)
+        if bias.numel() != N:
+            raise ValueError("convrot_linear_ex: bias must have N elements")
+    if workspace is None:
+        workspace = torch.empty(max(convrot_linear_workspace(M, K, N), 1), dtype=torch.uint8,
+                                device=x.device)
+    y = torch.empty((M, N), dtype=x.dtype, device=x.device) if out is None else out
+    _need(y, x.dtype, "out", 2)
+    _need(workspace, torch.uint8, "workspace")
+    if tuple(y.shape) != (M, N):
+        raise ValueError("convrot_linear_ex: output shape mismatch")
+    _call("convrot_linear_ex", _ptr(x), io, M, K, _ptr(wq), _ptr(w_scale), mode, N, group, _ptr(bias),
+          _ptr(y), _ptr(workspace), workspace.numel(), _stream(x))
     return y

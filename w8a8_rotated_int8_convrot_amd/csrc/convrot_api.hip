@@ -80,25 +80,140 @@ const char* convrot_last_error(void) { return g_last_error; }
 
 size_t convrot_prepare_weight_workspace(int64_t, int64_t) { return 256; }
 
-int convrot_prepare_weight(const void* w, int w_dtype, int64_t N, int64_t K, int group,
-                           int8_t* wq_out, float* w_scale_out, void* workspace, size_t ws_bytes,
-                           void* stream) {
-  const char* who = "convrot_prepare_weight";
+}  // extern "C"
+
+namespace {
+
+int check_io(int io_dtype, const char* who) {
+  if (io_dtype != CONVROT_BF16 && io_dtype != CONVROT_F16)
+    return fail(CONVROT_EUNSUPPORTED, "%s: activation/bias/output dtype %d (CONVROT_BF16 or CONVROT_F16)",
+                who, io_dtype);
+  return CONVROT_OK;
+}
+
+int check_scale_mode(int scale_mode, const char* who) {
+  if (scale_mode != CONVROT_SCALE_TENSOR && scale_mode != CONVROT_SCALE_ROW)
+    return fail(CONVROT_EUNSUPPORTED, "%s: weight scale mode %d (CONVROT_SCALE_TENSOR or CONVROT_SCALE_ROW)",
+                who, scale_mode);
+  return CONVROT_OK;
+}
+
+int prepare_weight_impl(const char* who, const void* w, int w_dtype, int64_t N, int64_t K, int group,
+                        int scale_mode, int8_t* wq_out, float* w_scale_out, void* workspace,
+                        size_t ws_bytes, void* stream) {
   if (int rc = check_group(group, K, who)) return rc;
+  if (int rc = check_scale_mode(scale_mode, who)) return rc;
   if (N < 1 || N > (int64_t(1) << 31) - 1)
     return fail(CONVROT_EINVAL, "%s: N=%lld must be in [1, 2^31)", who, static_cast<long long>(N));
-  if (w_dtype != CONVROT_F32 && w_dtype != CONVROT_BF16)
-    return fail(CONVROT_EUNSUPPORTED, "%s: weight dtype %d (CONVROT_F32 or CONVROT_BF16)", who, w_dtype);
+  if (w_dtype != CONVROT_F32 && w_dtype != CONVROT_BF16 && w_dtype != CONVROT_F16)
+    return fail(CONVROT_EUNSUPPORTED, "%s: weight dtype %d (CONVROT_F32, CONVROT_BF16 or CONVROT_F16)",
+                who, w_dtype);
   if (!w || !wq_out || !w_scale_out) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
   if (!aligned16(w) || !aligned16(wq_out) || (workspace && !aligned16(workspace)))
     return fail(CONVROT_EALIGN, "%s: w, wq_out and workspace must be 16-byte aligned", who);
   if (!workspace || ws_bytes < convrot_prepare_weight_workspace(N, K))
     return fail(CONVROT_EWORKSPACE, "%s: workspace of %zu bytes needed", who,
                 convrot_prepare_weight_workspace(N, K));
-  hipError_t e = convrot::launch_prepare_weight(w, w_dtype == CONVROT_BF16, N, K, group, wq_out,
-                                                w_scale_out, static_cast<uint32_t*>(workspace),
+  const int in = w_dtype == CONVROT_BF16 ? convrot::kInBf16
+               : w_dtype == CONVROT_F16  ? convrot::kInF16 : convrot::kInF32;
+  hipError_t e = convrot::launch_prepare_weight(w, in, scale_mode == CONVROT_SCALE_ROW, N, K, group,
+                                                wq_out, w_scale_out, static_cast<uint32_t*>(workspace),
                                                 static_cast<hipStream_t>(stream));
   return hip_status(e, who);
+}
+
+hipError_t rotate_quant_any(const void* x, int io_dtype, int64_t M, int64_t K, int group, int8_t* xq,
+                            float* x_scale, hipStream_t stream) {
+  const auto* xb = static_cast<const uint16_t*>(x);
+  return io_dtype == CONVROT_F16 ? convrot::launch_rotate_quant_f16(xb, M, K, group, xq, x_scale, stream)
+                                 : convrot::launch_rotate_quant(xb, M, K, group, xq, x_scale, stream);
+}
+
+int rotate_quant_impl(const char* who, const void* x, int io_dtype, int64_t M, int64_t K, int group,
+                      int8_t* xq, float* x_scale, void* stream) {
+  if (int rc = check_group(group, K, who)) return rc;
+  if (int rc = check_io(io_dtype, who)) return rc;
+  if (M < 0 || M > (int64_t(1) << 31) - 1)
+    return fail(CONVROT_EINVAL, "%s: M=%lld must be in [0, 2^31)", who, static_cast<long long>(M));
+  if (M == 0) return ok();
+  if (!x || !xq || !x_scale) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
+  if (!aligned16(x) || !aligned16(xq))
+    return fail(CONVROT_EALIGN, "%s: x and xq must be 16-byte aligned", who);
+  return hip_status(rotate_quant_any(x, io_dtype, M, K, group, xq, x_scale,
+                                     static_cast<hipStream_t>(stream)), who);
+}
+
+int gemm_dequant_impl(const char* who, const int8_t* xq, const float* x_scale, const int8_t* wq,
+                      const float* w_scale, int scale_mode, const void* bias, void* y, int io_dtype,
+                      int64_t M, int64_t N, int64_t K, void* stream) {
+  if (int rc = check_k(K, who)) return rc;
+  if (int rc = check_mn(M, N, who)) return rc;
+  if (int rc = check_io(io_dtype, who)) return rc;
+  if (int rc = check_scale_mode(scale_mode, who)) return rc;
+  if (M == 0) return ok();
+  if (!xq || !x_scale || !wq || !w_scale || !y) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
+  if (!aligned16(xq) || !aligned16(wq) || !aligned16(y))
+    return fail(CONVROT_EALIGN, "%s: xq, wq and y must be 16-byte aligned", who);
+  hipError_t e = convrot::launch_gemm_dequant_ex(xq, x_scale, wq, w_scale, scale_mode == CONVROT_SCALE_ROW,
+                                                 static_cast<const uint16_t*>(bias),
+                                                 static_cast<uint16_t*>(y), io_dtype == CONVROT_F16, M, N,
+                                                 K, static_cast<hipStream_t>(stream));
+  return hip_status(e, who);
+}
+
+int linear_impl(const char* who, const void* x_in, int io_dtype, int64_t M, int64_t K, const int8_t* wq,
+                const float* w_scale, int scale_mode, int64_t N, int group, const void* bias_in,
+                void* y_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (int rc = check_group(group, K, who)) return rc;
+  if (int rc = check_mn(M, N, who)) return rc;
+  if (int rc = check_io(io_dtype, who)) return rc;
+  if (int rc = check_scale_mode(scale_mode, who)) return rc;
+  if (M == 0) return ok();
+  if (!x_in || !wq || !w_scale || !y_out) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
+  if (!aligned16(x_in) || !aligned16(wq) || !aligned16(y_out) || (workspace && !aligned16(workspace)))
+    return fail(CONVROT_EALIGN, "%s: x, wq, y and workspace must be 16-byte aligned", who);
+  const int64_t S = workspace ? slice_rows(M, K, N, ws_bytes) : 0;
+  const int64_t need = M < 16 ? M : 16;
+  if (S < need)
+    return fail(CONVROT_EWORKSPACE, "%s: workspace of %zu bytes holds %lld rows; at least %lld needed "
+                "(convrot_linear_workspace gives %zu)", who, ws_bytes, static_cast<long long>(S),
+                static_cast<long long>(need), convrot_linear_workspace(M, K, N));
+  auto* xq = static_cast<int8_t*>(workspace);
+  auto* xs = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(static_cast<size_t>(S) * K, 256));
+  const auto* x = static_cast<const uint16_t*>(x_in);
+  auto* y = static_cast<uint16_t*>(y_out);
+  const auto* bias = static_cast<const uint16_t*>(bias_in);
+  const bool row = scale_mode == CONVROT_SCALE_ROW, f16 = io_dtype == CONVROT_F16;
+  auto s = static_cast<hipStream_t>(stream);
+  for (int64_t r0 = 0; r0 < M; r0 += S) {
+    const int64_t rows = (M - r0) < S ? (M - r0) : S;
+    hipError_t e = rotate_quant_any(x + r0 * K, io_dtype, rows, K, group, xq, xs, s);
+    if (e != hipSuccess) return hip_status(e, who);
+    e = convrot::launch_gemm_dequant_ex(xq, xs, wq, w_scale, row, bias, y + r0 * N, f16, rows, N, K, s);
+    if (e != hipSuccess) return hip_status(e, who);
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int convrot_prepare_weight(const void* w, int w_dtype, int64_t N, int64_t K, int group,
+                           int8_t* wq_out, float* w_scale_out, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  if (w_dtype == CONVROT_F16)
+    return fail(CONVROT_EUNSUPPORTED, "convrot_prepare_weight: weight dtype %d (CONVROT_F32 or "
+                "CONVROT_BF16; fp16 weights through convrot_prepare_weight_ex)", w_dtype);
+  return prepare_weight_impl("convrot_prepare_weight", w, w_dtype, N, K, group, CONVROT_SCALE_TENSOR,
+                             wq_out, w_scale_out, workspace, ws_bytes, stream);
+}
+
+int convrot_prepare_weight_ex(const void* w, int w_dtype, int64_t N, int64_t K, int group,
+                              int scale_mode, int8_t* wq_out, float* w_scale_out, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  return prepare_weight_impl("convrot_prepare_weight_ex", w, w_dtype, N, K, group, scale_mode, wq_out,
+                             w_scale_out, workspace, ws_bytes, stream);
 }
 
 size_t convrot_linear_workspace(int64_t M, int64_t K, int64_t N) {
@@ -109,17 +224,13 @@ size_t convrot_linear_workspace(int64_t M, int64_t K, int64_t N) {
 
 int convrot_rotate_quant(const void* x_bf16, int64_t M, int64_t K, int group, int8_t* xq,
                          float* x_scale, void* stream) {
-  const char* who = "convrot_rotate_quant";
-  if (int rc = check_group(group, K, who)) return rc;
-  if (M < 0 || M > (int64_t(1) << 31) - 1)
-    return fail(CONVROT_EINVAL, "%s: M=%lld must be in [0, 2^31)", who, static_cast<long long>(M));
-  if (M == 0) return ok();
-  if (!x_bf16 || !xq || !x_scale) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
-  if (!aligned16(x_bf16) || !aligned16(xq))
-    return fail(CONVROT_EALIGN, "%s: x and xq must be 16-byte aligned", who);
-  hipError_t e = convrot::launch_rotate_quant(static_cast<const uint16_t*>(x_bf16), M, K, group, xq,
-                                              x_scale, static_cast<hipStream_t>(stream));
-  return hip_status(e, who);
+  return rotate_quant_impl("convrot_rotate_quant", x_bf16, CONVROT_BF16, M, K, group, xq, x_scale,
+                           stream);
+}
+
+int convrot_rotate_quant_ex(const void* x, int x_dtype, int64_t M, int64_t K, int group, int8_t* xq,
+                            float* x_scale, void* stream) {
+  return rotate_quant_impl("convrot_rotate_quant_ex", x, x_dtype, M, K, group, xq, x_scale, stream);
 }
 
 int convrot_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64_t K,
@@ -138,50 +249,29 @@ int convrot_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, i
 int convrot_gemm_dequant(const int8_t* xq, const float* x_scale, const int8_t* wq,
                          const float* w_scale, const void* bias_bf16, void* y_bf16, int64_t M,
                          int64_t N, int64_t K, void* stream) {
-  const char* who = "convrot_gemm_dequant";
-  if (int rc = check_k(K, who)) return rc;
-  if (int rc = check_mn(M, N, who)) return rc;
-  if (M == 0) return ok();
-  if (!xq || !x_scale || !wq || !w_scale || !y_bf16) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
-  if (!aligned16(xq) || !aligned16(wq) || !aligned16(y_bf16))
-    return fail(CONVROT_EALIGN, "%s: xq, wq and y must be 16-byte aligned", who);
-  hipError_t e = convrot::launch_gemm_dequant(xq, x_scale, wq, w_scale,
-                                              static_cast<const uint16_t*>(bias_bf16),
-                                              static_cast<uint16_t*>(y_bf16), M, N, K,
-                                              static_cast<hipStream_t>(stream));
-  return hip_status(e, who);
+  return gemm_dequant_impl("convrot_gemm_dequant", xq, x_scale, wq, w_scale, CONVROT_SCALE_TENSOR,
+                           bias_bf16, y_bf16, CONVROT_BF16, M, N, K, stream);
+}
+
+int convrot_gemm_dequant_ex(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                            const float* w_scale, int scale_mode, const void* bias, void* y,
+                            int io_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_dequant_impl("convrot_gemm_dequant_ex", xq, x_scale, wq, w_scale, scale_mode, bias, y,
+                           io_dtype, M, N, K, stream);
 }
 
 int convrot_linear(const void* x_bf16, int64_t M, int64_t K, const int8_t* wq, const float* w_scale,
                    int64_t N, int group, const void* bias_bf16, void* y_bf16, void* workspace,
                    size_t ws_bytes, void* stream) {
-  const char* who = "convrot_linear";
-  if (int rc = check_group(group, K, who)) return rc;
-  if (int rc = check_mn(M, N, who)) return rc;
-  if (M == 0) return ok();
-  if (!x_bf16 || !wq || !w_scale || !y_bf16) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
-  if (!aligned16(x_bf16) || !aligned16(wq) || !aligned16(y_bf16) || (workspace && !aligned16(workspace)))
-    return fail(CONVROT_EALIGN, "%s: x, wq, y and workspace must be 16-byte aligned", who);
-  const int64_t S = workspace ? slice_rows(M, K, N, ws_bytes) : 0;
-  const int64_t need = M < 16 ? M : 16;
-  if (S < need)
-    return fail(CONVROT_EWORKSPACE, "%s: workspace of %zu bytes holds %lld rows; at least %lld needed "
-                "(convrot_linear_workspace gives %zu)", who, ws_bytes, static_cast<long long>(S),
-                static_cast<long long>(need), convrot_linear_workspace(M, K, N));
-  auto* xq = static_cast<int8_t*>(workspace);
-  auto* xs = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(static_cast<size_t>(S) * K, 256));
-  const auto* x = static_cast<const uint16_t*>(x_bf16);
-  auto* y = static_cast<uint16_t*>(y_bf16);
-  const auto* bias = static_cast<const uint16_t*>(bias_bf16);
-  auto s = static_cast<hipStream_t>(stream);
-  for (int64_t r0 = 0; r0 < M; r0 += S) {
-    const int64_t rows = (M - r0) < S ? (M - r0) : S;
-    hipError_t e = convrot::launch_rotate_quant(x + r0 * K, rows, K, group, xq, xs, s);
-    if (e != hipSuccess) return hip_status(e, who);
-    e = convrot::launch_gemm_dequant(xq, xs, wq, w_scale, bias, y + r0 * N, rows, N, K, s);
-    if (e != hipSuccess) return hip_status(e, who);
-  }
-  return ok();
+  return linear_impl("convrot_linear", x_bf16, CONVROT_BF16, M, K, wq, w_scale, CONVROT_SCALE_TENSOR, N,
+                     group, bias_bf16, y_bf16, workspace, ws_bytes, stream);
+}
+
+int convrot_linear_ex(const void* x, int io_dtype, int64_t M, int64_t K, const int8_t* wq,
+                      const float* w_scale, int scale_mode, int64_t N, int group, const void* bias,
+                      void* y, void* workspace, size_t ws_bytes, void* stream) {
+  return linear_impl("convrot_linear_ex", x, io_dtype, M, K, wq, w_scale, scale_mode, N, group, bias, y,
+                     workspace, ws_bytes, stream);
 }
 
 int convrot_probe_mfma_i8(const int8_t* a, int64_t a_bytes, const int8_t* b, int64_t b_bytes,

@@ -21,11 +21,16 @@ constexpr int64_t kMaxK = 131072;
 // fp32 scales.  group is 128 or 256; K % group == 0.
 hipError_t launch_rotate_quant(const uint16_t* x, int64_t M, int64_t K, int group,
                                int8_t* q, float* scale, hipStream_t stream);
+// The same for an IEEE binary16 activation (bits passed as uint16_t).
+hipError_t launch_rotate_quant_f16(const uint16_t* x, int64_t M, int64_t K, int group,
+                                   int8_t* q, float* scale, hipStream_t stream);
 
-// Tensorwise weight preparation.  `in_bf16` selects the input type (fp32
-// otherwise).  `amax_cell` is one 4-byte device word of scratch.
-hipError_t launch_prepare_weight(const void* w, bool in_bf16, int64_t N, int64_t K, int group,
-                                 int8_t* wq, float* w_scale, uint32_t* amax_cell,
+// Weight preparation.  in_dtype: kInF32, kInBf16 or kInF16.  Tensorwise (one
+// scale; `amax_cell` is one 4-byte device word of scratch) or, with
+// row_scale, one scale per output channel (w_scale [N]; no scratch).
+constexpr int kInF32 = 0, kInBf16 = 1, kInF16 = 2;
+hipError_t launch_prepare_weight(const void* w, int in_dtype, bool row_scale, int64_t N, int64_t K,
+                                 int group, int8_t* wq, float* w_scale, uint32_t* amax_cell,
                                  hipStream_t stream);
 
 // ---------------------------------------------------------------- GEMM
@@ -35,6 +40,13 @@ hipError_t launch_prepare_weight(const void* w, bool in_bf16, int64_t N, int64_t
 hipError_t launch_gemm_dequant(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                const float* w_scale, const uint16_t* bias, uint16_t* y,
                                int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// Variants: one weight scale per output channel (row_scale: w_scale [N]) and
+// fp16 in place of bf16 for the bias and the output (out_f16).
+hipError_t launch_gemm_dequant_ex(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                  const float* w_scale, bool row_scale, const uint16_t* bias,
+                                  uint16_t* y, bool out_f16, int64_t M, int64_t N, int64_t K,
+                                  hipStream_t stream);
 
 // Same main loop with the raw int32 products stored.
 hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,

@@ -203,13 +203,33 @@ __device__ inline int out_lds_offset(int m, int n) {
   return m * (T::BN * 2) + (((n >> 3) ^ (m & kMask)) << 4) + ((n & 7) << 1);
 }
 
-template <class T, bool DEQUANT>
+// Epilogue modes: raw int32 products, or dequant + bias to bf16 / fp16 with
+// one weight scale (tensorwise) or one per output channel (row-wise).
+enum Epi { kEpiI32 = 0, kEpiBf16 = 1, kEpiBf16Row = 2, kEpiF16 = 3, kEpiF16Row = 4 };
+
+__device__ inline uint32_t pack_f16x2(float a, float b) {
+  const _Float16 ha = static_cast<_Float16>(a);   // v_cvt_f16_f32: round to nearest even
+  const _Float16 hb = static_cast<_Float16>(b);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ha)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hb)) << 16);
+}
+__device__ inline float f16_bits_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
+}
+__device__ inline float f16_bits_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+template <class T, int EPI>
 __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
     const int8_t* __restrict__ wq, const int8_t* __restrict__ xq, int M, int N, int K,
     int tiles_n, int tiles_m, const float* __restrict__ x_scale,
     const float* __restrict__ w_scale, const uint16_t* __restrict__ bias,
     void* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) char lds[T::kLdsBytes];
+  constexpr bool DEQUANT = EPI != kEpiI32;
+  constexpr bool kRowScale = EPI == kEpiBf16Row || EPI == kEpiF16Row;
+  constexpr bool kF16 = EPI == kEpiF16 || EPI == kEpiF16Row;
 
   int tn, tm;
   tile_coords<T>(tiles_n, tiles_m, tn, tm);
@@ -281,6 +301,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
 #pragma unroll
   for (int j = 0; j < T::TM; ++j)
     alpha[j] = DEQUANT ? x_scale[min(m0 + m_lane0 + j * T::MF, M - 1)] : 0.0f;
+  (void)w_scale;
 
   // Fragments are double-buffered per MFMA k step (a "unit": 32 bytes of K
   // for 32x32x32, 64 for 16x16x64): while the MFMAs of one unit run from one
@@ -436,10 +457,28 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
     uint16_t* y = static_cast<uint16_t*>(out);
     // Scales and bias for this lane's outputs: every load is issued before
     // the first one is used, so their latency is paid once per tile.
-    const float sw = *w_scale;
+    const float sw = kRowScale ? 1.0f : *w_scale;
     // bias of n = n0 + n_loc + i*MF + 8*g + e, e = 0..3: 8-byte loads when the
     // four values are in range and aligned, else element by element
     uint2 bias4[T::TN][kGroups];
+    // row-wise weight scales of the same four channels
+    float4 ws4[kRowScale ? T::TN : 1][kRowScale ? kGroups : 1];
+    if constexpr (kRowScale) {
+      const bool ws_vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(w_scale) & 15) == 0;
+#pragma unroll
+      for (int i = 0; i < T::TN; ++i) {
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+          const int n = n0 + n_loc + i * T::MF + 8 * g;
+          if (ws_vec) {
+            ws4[i][g] = *reinterpret_cast<const float4*>(w_scale + min(n, N - 4));
+          } else {
+            ws4[i][g] = make_float4(w_scale[min(n, N - 1)], w_scale[min(n + 1, N - 1)],
+                                    w_scale[min(n + 2, N - 1)], w_scale[min(n + 3, N - 1)]);
+          }
+        }
+      }
+    }
     const bool bias_vec = bias != nullptr && (N & 3) == 0 && (reinterpret_cast<uintptr_t>(bias) & 7) == 0;
 #pragma unroll
     for (int i = 0; i < T::TN; ++i) {
@@ -468,16 +507,38 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
 #pragma unroll
       for (int g = 0; g < kGroups; ++g) {
         const int nl = n_loc + i * T::MF + 8 * g;
-        const float b[4] = {__uint_as_float(bias4[i][g].x << 16), __uint_as_float(bias4[i][g].x & 0xffff0000u),
-                            __uint_as_float(bias4[i][g].y << 16), __uint_as_float(bias4[i][g].y & 0xffff0000u)};
+        float b[4];
+        if constexpr (kF16) {
+          b[0] = f16_bits_lo(bias4[i][g].x); b[1] = f16_bits_hi(bias4[i][g].x);
+          b[2] = f16_bits_lo(bias4[i][g].y); b[3] = f16_bits_hi(bias4[i][g].y);
+        } else {
+          b[0] = __uint_as_float(bias4[i][g].x << 16); b[1] = __uint_as_float(bias4[i][g].x & 0xffff0000u);
+          b[2] = __uint_as_float(bias4[i][g].y << 16); b[3] = __uint_as_float(bias4[i][g].y & 0xffff0000u);
+        }
 #pragma unroll
         for (int j = 0; j < T::TM; ++j) {
           float v[4];
+          if constexpr (kRowScale) {
+            // alpha = s_x[m] * s_w[n], one fp32 product per output
+            const float sc[4] = {ws4[i][g].x, ws4[i][g].y, ws4[i][g].z, ws4[i][g].w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = __builtin_fmaf(static_cast<float>(acc[i][j][4 * g + e]), alpha[j], b[e]);
+            for (int e = 0; e < 4; ++e)
+              v[e] = __builtin_fmaf(static_cast<float>(acc[i][j][4 * g + e]), alpha[j] * sc[e], b[e]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v[e] = __builtin_fmaf(static_cast<float>(acc[i][j][4 * g + e]), alpha[j], b[e]);
+          }
+          if constexpr (kF16) {
+            // the output is fp16_rne of the fp32 result: keep v in fp32 here,
+            // or the compiler fuses fma and conversion into v_fma_mixlo_f16,
+            // which rounds the exact value to fp16 once
+#pragma unroll
+            for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(v[e]));
+          }
           *reinterpret_cast<uint2*>(lds + out_lds_offset<T>(m_loc + j * T::MF, nl)) =
-              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+              kF16 ? make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]))
+                   : make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
       }
     }
@@ -532,14 +593,14 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
   }
 }
 
-template <class T, bool DEQUANT>
+template <class T, int EPI>
 hipError_t launch_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
                        const float* w_scale, const uint16_t* bias, void* out, int64_t M,
                        int64_t N, int64_t K, hipStream_t stream) {
   const int tiles_n = static_cast<int>((N + T::BN - 1) / T::BN);
   const int tiles_m = static_cast<int>((M + T::BM - 1) / T::BM);
   const int64_t blocks = static_cast<int64_t>(tiles_n) * tiles_m;
-  hipLaunchKernelGGL((gemm_i8_kernel<T, DEQUANT>), dim3(static_cast<uint32_t>(blocks)),
+  hipLaunchKernelGGL((gemm_i8_kernel<T, EPI>), dim3(static_cast<uint32_t>(blocks)),
                      dim3(T::kThreads), 0, stream, wq, xq, static_cast<int>(M), static_cast<int>(N),
                      static_cast<int>(K), tiles_n, tiles_m, x_scale, w_scale, bias, out);
   return hipGetLastError();
@@ -579,19 +640,19 @@ int pick_tile(int64_t M, int64_t N) {
   return tile_cost(M, N, 384, 192) < tile_cost(M, N, 256, 256) ? 6 : 1;
 }
 
-template <bool DEQUANT>
+template <int EPI>
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                        const float* w_scale, const uint16_t* bias, void* out, int64_t M,
                        int64_t N, int64_t K, hipStream_t stream) {
   int t = forced_tile();
   if (t == 0) t = pick_tile(M, N);
-  if (t == 1) return launch_tile<TileBig, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
-  if (t == 2) return launch_tile<TileBig8, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
-  if (t == 4) return launch_tile<TileWide, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
-  if (t == 5) return launch_tile<TileSkinny, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
-  if (t == 6) return launch_tile<TileWide128, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
-  if (t == 7) return launch_tile<TileSkinny16, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
-  return launch_tile<TileMid, DEQUANT>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 1) return launch_tile<TileBig, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 2) return launch_tile<TileBig8, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 4) return launch_tile<TileWide, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 5) return launch_tile<TileSkinny, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 6) return launch_tile<TileWide128, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 7) return launch_tile<TileSkinny16, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  return launch_tile<TileMid, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
 }
 
 }  // namespace
@@ -599,14 +660,25 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
 hipError_t launch_gemm_dequant(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                const float* w_scale, const uint16_t* bias, uint16_t* y,
                                int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  return launch_gemm_dequant_ex(xq, x_scale, wq, w_scale, false, bias, y, false, M, N, K, stream);
+}
+
+hipError_t launch_gemm_dequant_ex(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                  const float* w_scale, bool row_scale, const uint16_t* bias,
+                                  uint16_t* y, bool out_f16, int64_t M, int64_t N, int64_t K,
+                                  hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  return launch_gemm<true>(xq, x_scale, wq, w_scale, bias, y, M, N, K, stream);
+  if (out_f16)
+    return row_scale ? launch_gemm<kEpiF16Row>(xq, x_scale, wq, w_scale, bias, y, M, N, K, stream)
+                     : launch_gemm<kEpiF16>(xq, x_scale, wq, w_scale, bias, y, M, N, K, stream);
+  return row_scale ? launch_gemm<kEpiBf16Row>(xq, x_scale, wq, w_scale, bias, y, M, N, K, stream)
+                   : launch_gemm<kEpiBf16>(xq, x_scale, wq, w_scale, bias, y, M, N, K, stream);
 }
 
 hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc, int64_t M,
                            int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  return launch_gemm<false>(xq, nullptr, wq, nullptr, nullptr, acc, M, N, K, stream);
+  return launch_gemm<kEpiI32>(xq, nullptr, wq, nullptr, nullptr, acc, M, N, K, stream);
 }
 
 }  // namespace convrot

@@ -40,15 +40,32 @@ enum Mode { kActQuant = 0, kWeightAbsmax = 1, kWeightQuant = 2 };
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// IEEE binary16 -> fp32 is exact (v_cvt_f32_f16)
+__device__ inline float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
+}
+__device__ inline float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+// the two 16-bit input formats: bf16 bits (uint16_t) and IEEE binary16 (_Float16)
+template <typename In> __device__ inline float in_lo(uint32_t w);
+template <typename In> __device__ inline float in_hi(uint32_t w);
+template <> __device__ inline float in_lo<uint16_t>(uint32_t w) { return bf16_lo(w); }
+template <> __device__ inline float in_hi<uint16_t>(uint32_t w) { return bf16_hi(w); }
+template <> __device__ inline float in_lo<_Float16>(uint32_t w) { return f16_lo(w); }
+template <> __device__ inline float in_hi<_Float16>(uint32_t w) { return f16_hi(w); }
 
 // Load 8 consecutive inputs as fp32.
-__device__ inline void load8(const uint16_t* p, float (&v)[8]) {
+template <typename In16>
+__device__ inline void load8_16(const In16* p, float (&v)[8]) {
   const uint4 w = *reinterpret_cast<const uint4*>(p);
-  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
-  v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
-  v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+  v[0] = in_lo<In16>(w.x); v[1] = in_hi<In16>(w.x);
+  v[2] = in_lo<In16>(w.y); v[3] = in_hi<In16>(w.y);
+  v[4] = in_lo<In16>(w.z); v[5] = in_hi<In16>(w.z);
+  v[6] = in_lo<In16>(w.w); v[7] = in_hi<In16>(w.w);
 }
+__device__ inline void load8(const uint16_t* p, float (&v)[8]) { load8_16(p, v); }
+__device__ inline void load8(const _Float16* p, float (&v)[8]) { load8_16(p, v); }
 __device__ inline void load8(const float* p, float (&v)[8]) {
   const float4 a = *reinterpret_cast<const float4*>(p);
   const float4 b = *reinterpret_cast<const float4*>(p + 4);
@@ -206,9 +223,9 @@ constexpr int kMaxBlocksPerWg = 256;                 // one block per thread
 constexpr int kMaxBlockK = kMaxBlocksPerWg * kBlockElems;
 constexpr int64_t kSmallBatchElems = int64_t{1} << 21;
 
-template <int G>
+template <int G, typename In16>
 __global__ __launch_bounds__(256) void rotq_block_kernel(
-    const uint16_t* __restrict__ x, int64_t M, int K, int rows_per_wg,
+    const In16* __restrict__ x, int64_t M, int K, int rows_per_wg,
     int8_t* __restrict__ q, float* __restrict__ scale) {
   // bf16 input tile: block b occupies 16 chunks of 16 bytes; chunk j is stored
   // at j ^ (b & 15) so that 32 lanes reading chunk j of 32 consecutive blocks
@@ -246,10 +263,10 @@ __global__ __launch_bounds__(256) void rotq_block_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const uint4 w = tile[b * 16 + (j ^ (b & 15))];
-      v[8 * j + 0] = bf16_lo(w.x); v[8 * j + 1] = bf16_hi(w.x);
-      v[8 * j + 2] = bf16_lo(w.y); v[8 * j + 3] = bf16_hi(w.y);
-      v[8 * j + 4] = bf16_lo(w.z); v[8 * j + 5] = bf16_hi(w.z);
-      v[8 * j + 6] = bf16_lo(w.w); v[8 * j + 7] = bf16_hi(w.w);
+      v[8 * j + 0] = in_lo<In16>(w.x); v[8 * j + 1] = in_hi<In16>(w.x);
+      v[8 * j + 2] = in_lo<In16>(w.y); v[8 * j + 3] = in_hi<In16>(w.y);
+      v[8 * j + 4] = in_lo<In16>(w.z); v[8 * j + 5] = in_hi<In16>(w.z);
+      v[8 * j + 6] = in_lo<In16>(w.w); v[8 * j + 7] = in_hi<In16>(w.w);
     }
 #pragma unroll
     for (int h = 1; h < kBlockElems; h <<= 1) {
@@ -392,8 +409,11 @@ hipError_t dispatch_group(int group, const In* x, int64_t rows, int64_t K, int8_
 
 }  // namespace
 
-hipError_t launch_rotate_quant(const uint16_t* x, int64_t M, int64_t K, int group, int8_t* q,
-                               float* scale, hipStream_t stream) {
+namespace {
+
+template <typename In16>
+hipError_t rotate_quant_16(const In16* x, int64_t M, int64_t K, int group, int8_t* q,
+                           float* scale, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   // Small batches (up to 2^21 elements, e.g. 512 x 4096): one lane per
   // 128-element block leaves each lane a long serial chain of arithmetic and
@@ -409,27 +429,55 @@ hipError_t launch_rotate_quant(const uint16_t* x, int64_t M, int64_t K, int grou
     const int rows_per_wg = static_cast<int>(share < fit ? share : fit);
     const int64_t wgs = (M + rows_per_wg - 1) / rows_per_wg;
     if (group == 128)
-      hipLaunchKernelGGL(rotq_block_kernel<128>, dim3(static_cast<uint32_t>(wgs)), dim3(256), 0, stream,
-                         x, M, static_cast<int>(K), rows_per_wg, q, scale);
+      hipLaunchKernelGGL((rotq_block_kernel<128, In16>), dim3(static_cast<uint32_t>(wgs)), dim3(256), 0,
+                         stream, x, M, static_cast<int>(K), rows_per_wg, q, scale);
     else
-      hipLaunchKernelGGL(rotq_block_kernel<256>, dim3(static_cast<uint32_t>(wgs)), dim3(256), 0, stream,
-                         x, M, static_cast<int>(K), rows_per_wg, q, scale);
+      hipLaunchKernelGGL((rotq_block_kernel<256, In16>), dim3(static_cast<uint32_t>(wgs)), dim3(256), 0,
+                         stream, x, M, static_cast<int>(K), rows_per_wg, q, scale);
     return hipGetLastError();
   }
-  return dispatch_group<uint16_t, kActQuant>(group, x, M, K, q, scale, nullptr, stream);
+  return dispatch_group<In16, kActQuant>(group, x, M, K, q, scale, nullptr, stream);
 }
 
-hipError_t launch_prepare_weight(const void* w, bool in_bf16, int64_t N, int64_t K, int group,
-                                 int8_t* wq, float* w_scale, uint32_t* amax_cell,
+}  // namespace
+
+hipError_t launch_rotate_quant(const uint16_t* x, int64_t M, int64_t K, int group, int8_t* q,
+                               float* scale, hipStream_t stream) {
+  return rotate_quant_16(x, M, K, group, q, scale, stream);
+}
+
+hipError_t launch_rotate_quant_f16(const uint16_t* x, int64_t M, int64_t K, int group, int8_t* q,
+                                   float* scale, hipStream_t stream) {
+  return rotate_quant_16(reinterpret_cast<const _Float16*>(x), M, K, group, q, scale, stream);
+}
+
+hipError_t launch_prepare_weight(const void* w, int in_dtype, bool row_scale, int64_t N, int64_t K,
+                                 int group, int8_t* wq, float* w_scale, uint32_t* amax_cell,
                                  hipStream_t stream) {
+  // One scale per output channel: every weight row is quantized exactly like
+  // a token (the same rotation, absmax, scale and codes).
+  if (row_scale) {
+    if (in_dtype == kInBf16)
+      return rotate_quant_16(static_cast<const uint16_t*>(w), N, K, group, wq, w_scale, stream);
+    if (in_dtype == kInF16)
+      return rotate_quant_16(static_cast<const _Float16*>(w), N, K, group, wq, w_scale, stream);
+    return dispatch_group<float, kActQuant>(group, static_cast<const float*>(w), N, K, wq, w_scale,
+                                            nullptr, stream);
+  }
   hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(1), 0, stream, amax_cell);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (in_bf16) {
+  if (in_dtype == kInBf16) {
     const auto* x = static_cast<const uint16_t*>(w);
     e = dispatch_group<uint16_t, kWeightAbsmax>(group, x, N, K, nullptr, nullptr, amax_cell, stream);
     if (e != hipSuccess) return e;
     return dispatch_group<uint16_t, kWeightQuant>(group, x, N, K, wq, w_scale, amax_cell, stream);
+  }
+  if (in_dtype == kInF16) {
+    const auto* x = static_cast<const _Float16*>(w);
+    e = dispatch_group<_Float16, kWeightAbsmax>(group, x, N, K, nullptr, nullptr, amax_cell, stream);
+    if (e != hipSuccess) return e;
+    return dispatch_group<_Float16, kWeightQuant>(group, x, N, K, wq, w_scale, amax_cell, stream);
   }
   const auto* x = static_cast<const float*>(w);
   e = dispatch_group<float, kWeightAbsmax>(group, x, N, K, nullptr, nullptr, amax_cell, stream);
