@@ -23,7 +23,8 @@ CPU oracle timed on a bounded sample of token rows.  Beside them:
                 fraction of it;
   paths         the HBM-bound steps against 8 TB/s: rotate+quant of this
                 workload, and the few-token layer (M=16, K=4096, N=12288)
-                with its weight read from HBM on every call.
+                with its weight read from HBM on every call; and the fp16 /
+                row-wise-scale variant of the whole layer at this shape.
 """
 import argparse
 import hashlib
@@ -240,6 +241,22 @@ def main():
 
     small = small_m_paths(binding, synth, np, torch, dev, stream, g, args.steps)
 
+    # the same layer in fp16 with one weight scale per output channel
+    # (convrot_linear_ex), timed the same way as the step
+    w_dev = torch.from_numpy(L.w).to(dev)
+    wq_r, s_r = binding.convrot_prepare_weight_ex(w_dev, g, "row")
+    del w_dev
+    x16, b16 = x.to(torch.float16), bias.to(torch.float16)
+    y16 = torch.empty((M, N), dtype=torch.float16, device=dev)
+    for _ in range(5):
+        binding.convrot_linear_ex(x16, wq_r, s_r, g, b16, out=y16, workspace=ws)
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        binding.convrot_linear_ex(x16, wq_r, s_r, g, b16, out=y16, workspace=ws)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    var_ms = ev[0].elapsed_time(ev[1]) / args.steps
+
     ops = 2.0 * M * N * K
     value = ops / step_s / 1e12
     achieved = ops / (gemm_ms * 1e-3) / 1e12
@@ -282,6 +299,10 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(rq_bytes / (rotq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         **small,
+        "linear_f16_rowscale": {"entry": "convrot_linear_ex", "workload": "the bench shape with fp16 "
+                                "activation, bias and output and one weight scale per output channel",
+                                "ms": round(var_ms, 5), "value": round(ops / (var_ms * 1e-3) / 1e12, 2),
+                                "unit": "TOPS"},
     }
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)

@@ -461,24 +461,16 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
     // bias of n = n0 + n_loc + i*MF + 8*g + e, e = 0..3: 8-byte loads when the
     // four values are in range and aligned, else element by element
     uint2 bias4[T::TN][kGroups];
-    // row-wise weight scales of the same four channels
-    float4 ws4[kRowScale ? T::TN : 1][kRowScale ? kGroups : 1];
-    if constexpr (kRowScale) {
-      const bool ws_vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(w_scale) & 15) == 0;
-#pragma unroll
-      for (int i = 0; i < T::TN; ++i) {
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
-          const int n = n0 + n_loc + i * T::MF + 8 * g;
-          if (ws_vec) {
-            ws4[i][g] = *reinterpret_cast<const float4*>(w_scale + min(n, N - 4));
-          } else {
-            ws4[i][g] = make_float4(w_scale[min(n, N - 1)], w_scale[min(n + 1, N - 1)],
-                                    w_scale[min(n + 2, N - 1)], w_scale[min(n + 3, N - 1)]);
-          }
-        }
-      }
-    }
+    // row-wise weight scales of the same four channels, loaded one MFMA row
+    // block (i) at a time below: all of them at once would not fit beside
+    // the accumulators
+    const bool ws_vec = kRowScale && (N & 3) == 0 && (reinterpret_cast<uintptr_t>(w_scale) & 15) == 0;
+    auto load_ws = [&](int i, int g) -> float4 {
+      const int n = n0 + n_loc + i * T::MF + 8 * g;
+      if (ws_vec) return *reinterpret_cast<const float4*>(w_scale + min(n, N - 4));
+      return make_float4(w_scale[min(n, N - 1)], w_scale[min(n + 1, N - 1)],
+                         w_scale[min(n + 2, N - 1)], w_scale[min(n + 3, N - 1)]);
+    };
     const bool bias_vec = bias != nullptr && (N & 3) == 0 && (reinterpret_cast<uintptr_t>(bias) & 7) == 0;
 #pragma unroll
     for (int i = 0; i < T::TN; ++i) {
@@ -504,6 +496,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
     wait_vm_barrier<0>();
 #pragma unroll
     for (int i = 0; i < T::TN; ++i) {
+      float4 ws4[kRowScale ? kGroups : 1];
+      if constexpr (kRowScale) {
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) ws4[g] = load_ws(i, g);
+      }
 #pragma unroll
       for (int g = 0; g < kGroups; ++g) {
         const int nl = n_loc + i * T::MF + 8 * g;
@@ -520,7 +517,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
           float v[4];
           if constexpr (kRowScale) {
             // alpha = s_x[m] * s_w[n], one fp32 product per output
-            const float sc[4] = {ws4[i][g].x, ws4[i][g].y, ws4[i][g].z, ws4[i][g].w};
+            const float sc[4] = {ws4[g].x, ws4[g].y, ws4[g].z, ws4[g].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               v[e] = __builtin_fmaf(static_cast<float>(acc[i][j][4 * g + e]), alpha[j] * sc[e], b[e]);
