@@ -155,6 +155,53 @@ def small_m_paths(binding, synth, np, torch, dev, stream, g, steps):
     }
 
 
+def streamed_path(binding, torch, dev, stream, x, wq, s_w, g, bias, n_layers=8, reps=3):
+    """Eight layers of the bench shape whose int8 weights stay in pinned host
+    memory (convrot_linear_streamed: each weight copied over the host link
+    into one of two device slots while the previous layer computes), against
+    the same eight layers with resident weights, and against the plain
+    host-to-device copy of the eight weights."""
+    M, K = x.shape
+    N = wq.shape[0]
+    hosts = [wq.cpu().pin_memory() for _ in range(n_layers)]
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(n_layers)]
+    layers = [{"x": x, "wq_host": h, "w_scale": s_w, "group": g, "bias": bias, "out": o}
+              for h, o in zip(hosts, outs)]
+    slots = torch.empty(2 * binding.convrot_stream_slot_bytes(layers), dtype=torch.uint8, device=dev)
+    ws = torch.empty(binding.convrot_linear_workspace(M, K, N), dtype=torch.uint8, device=dev)
+    # both on created streams: HIP's null stream orders itself against every
+    # other stream and would serialise the copies with the compute
+    cs, comp = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(comp):
+            fn()
+            torch.cuda.synchronize()
+            ev[0].record(comp)
+            for _ in range(reps):
+                fn()
+            ev[1].record(comp)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    t_stream = timed(lambda: binding.convrot_linear_streamed(layers, slots=slots, workspace=ws, copy_stream=cs))
+    t_res = timed(lambda: [binding.convrot_linear(x, wq, s_w, g, bias, out=o, workspace=ws) for o in outs])
+    dst = [slots[:N * K], slots[slots.numel() // 2:slots.numel() // 2 + N * K]]
+    t_copy = timed(lambda: [dst[i % 2].copy_(h.view(torch.uint8).view(-1), non_blocking=True)
+                            for i, h in enumerate(hosts)])      # on `comp`: one stream, back to back
+    wbytes = n_layers * N * K
+    return {"entry": "convrot_linear_streamed", "layers": n_layers,
+            "workload": f"{n_layers} layers of the bench shape, int8 weights ({N * K / 1e6:.1f} MB each) "
+                        "in pinned host memory",
+            "ms_per_layer": round(t_stream / n_layers, 4),
+            "resident_ms_per_layer": round(t_res / n_layers, 4),
+            "copy_only_ms_per_layer": round(t_copy / n_layers, 4),
+            "weight_GBps": round(wbytes / (t_stream * 1e-3) / 1e9, 1),
+            "copy_only_GBps": round(wbytes / (t_copy * 1e-3) / 1e9, 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -240,6 +287,7 @@ def main():
     probe_tops = probe_blocks * 4 * probe_iters * 16 * 65536 / (probe_ms * 1e-3) / 1e12
 
     small = small_m_paths(binding, synth, np, torch, dev, stream, g, args.steps)
+    streamed = streamed_path(binding, torch, dev, stream, x, wq, s_w, g, bias)
 
     # the same layer in fp16 with one weight scale per output channel
     # (convrot_linear_ex), timed the same way as the step
@@ -299,6 +347,7 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(rq_bytes / (rotq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         **small,
+        "streamed_weights": streamed,
         "linear_f16_rowscale": {"entry": "convrot_linear_ex", "workload": "the bench shape with fp16 "
                                 "activation, bias and output and one weight scale per output channel",
                                 "ms": round(var_ms, 5), "value": round(ops / (var_ms * 1e-3) / 1e12, 2),

@@ -188,6 +188,50 @@ int convrot_linear_ex(const void *x, int io_dtype, int64_t M, int64_t K, const i
                       const void *bias, void *y, void *workspace, size_t ws_bytes,
                       void *stream);
 
+/* ---------------------------------------------------------------- streamed weights
+ * Page "int8 Compute", "Partially loaded models": a layer whose weight is
+ * still in host RAM is copied to the GPU as int8 for each step (half the bytes
+ * of the unpacked weight) and computed exactly like a resident one, and the
+ * result is bit-identical.  convrot_linear_streamed runs a sequence of layers
+ * whose int8 weights live in pinned host memory: each weight is copied into
+ * one of two device slots on `copy_stream` while the previous layer computes
+ * on `stream`, and each layer then runs exactly as convrot_linear on its slot
+ * (same kernels, same bits).  A slot is refilled only after the layer that
+ * used it two steps earlier has finished; the first copy waits for the work
+ * already queued on `stream`.  The layers run in order on `stream`; when
+ * `stream` reaches the end of the call every output is complete and nothing
+ * of the call is left on `copy_stream`.  Copies overlap compute only when
+ * both streams are created streams: HIP's null stream (NULL) orders itself
+ * against the other streams, which serialises copy and compute (the results
+ * are the same). */
+typedef struct convrot_stream_layer {
+    const void   *x;         /* device, bf16 [M, K] */
+    int64_t       M, K, N;
+    const int8_t *wq_host;   /* HOST, pinned (hipHostMalloc or torch pin_memory), int8 [N, K],
+                                as written by convrot_prepare_weight */
+    const float  *w_scale;   /* device, 1 float */
+    int           group;     /* 128 or 256 */
+    const void   *bias;      /* device, bf16 [N], or NULL */
+    void         *y;         /* device, bf16 [M, N] */
+} convrot_stream_layer;
+
+/* Bytes one weight slot needs: the largest N*K of the layers, rounded up to
+ * 256.  0 if n_layers < 1 or layers is NULL. */
+size_t convrot_stream_slot_bytes(const convrot_stream_layer *layers, int n_layers);
+
+/* layers: host array of n_layers >= 0 descriptors (read during the call only).
+ * slots: device, 2 * slot_bytes, 16-byte aligned, slot_bytes >= every N*K.
+ * workspace / ws_bytes: as for convrot_linear, enough for every layer (the
+ * layers run one after another on `stream` and share it).
+ * Every layer is checked before anything is queued: the convrot_linear rules
+ * (CONVROT_EINVAL, CONVROT_EUNSUPPORTED, CONVROT_EALIGN, CONVROT_EWORKSPACE),
+ * a slot too small (CONVROT_EWORKSPACE) and a weight that is not pinned host
+ * memory (CONVROT_EINVAL); nothing is queued then.  HIP errors while queueing
+ * return CONVROT_EHIP (work queued so far stays queued). */
+int convrot_linear_streamed(const convrot_stream_layer *layers, int n_layers,
+                            void *slots, size_t slot_bytes, void *workspace, size_t ws_bytes,
+                            void *copy_stream, void *stream);
+
 /* ---------------------------------------------------------------- measurement aid
  * Not a step of the layer and defined by no page: it exists so that a
  * benchmark can state the rate the matrix cores sustain on this machine,

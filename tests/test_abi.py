@@ -167,3 +167,20 @@ def test_variant_argument_errors(lib):
     assert lib.convrot_linear_ex(A + 2, F16, 64, 512, A, A, 1, 64, 128, None, A, A, 1 << 20, None) == EALIGN
     assert lib.convrot_gemm_dequant_ex(A, A, A, A, 1, None, A + 4, F16, 4, 4, 256, None) == EALIGN
     assert lib.convrot_linear_ex(None, F16, 0, 512, None, None, 1, 64, 128, None, None, None, 0, None) == OK
+
+
+def test_streamed_argument_errors(lib, binding):
+    import ctypes
+    L = binding.StreamLayer(A, 64, 512, 64, A, A, 128, None, A)
+    arr = (binding.StreamLayer * 2)(L, L)
+    f = lib.convrot_linear_streamed
+    assert f(None, 2, A, 1 << 16, A, 1 << 20, None, None) == EINVAL
+    assert f(arr, -1, A, 1 << 16, A, 1 << 20, None, None) == EINVAL
+    assert f(arr, 0, None, 0, None, 0, None, None) == OK
+    assert f(arr, 2, A + 8, 1 << 16, A, 1 << 20, None, None) == EALIGN
+    assert f(arr, 2, A, 1024, A, 1 << 20, None, None) == EWORKSPACE          # slot < N*K
+    assert f(arr, 2, A, 1 << 16, A, 100, None, None) == EWORKSPACE            # workspace
+    bad = (binding.StreamLayer * 1)(binding.StreamLayer(A, 64, 512, 64, A, A, 64, None, A))
+    assert f(bad, 1, A, 1 << 16, A, 1 << 20, None, None) == EUNSUPPORTED       # group
+    assert lib.convrot_stream_slot_bytes(arr, 2) == 64 * 512
+    assert ctypes.sizeof(binding.StreamLayer) == 72

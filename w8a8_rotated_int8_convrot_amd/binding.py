@@ -42,6 +42,8 @@ SIGNATURES = {
     "convrot_rotate_quant_ex": ([_P, _I, _I64, _I64, _I, _P, _P, _P], _I),
     "convrot_gemm_dequant_ex": ([_P, _P, _P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _P], _I),
     "convrot_linear_ex": ([_P, _I, _I64, _I64, _P, _P, _I, _I64, _I, _P, _P, _P, _SZ, _P], _I),
+    "convrot_stream_slot_bytes": ([_P, _I], _SZ),
+    "convrot_linear_streamed": ([_P, _I, _P, _SZ, _P, _SZ, _P, _P], _I),
 }
 
 
@@ -330,3 +332,61 @@ def convrot_linear_ex(x, wq, w_scale, group, bias=None, out=None, workspace=None
     _call("convrot_linear_ex", _ptr(x), io, M, K, _ptr(wq), _ptr(w_scale), mode, N, group, _ptr(bias),
           _ptr(y), _ptr(workspace), workspace.numel(), _stream(x))
     return y
+
+
+# ---------------------------------------------------------------- streamed weights
+
+class StreamLayer(ctypes.Structure):
+    """Mirror of ``convrot_stream_layer`` (include/convrot.h)."""
+    _fields_ = [("x", ctypes.c_void_p), ("M", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("wq_host", ctypes.c_void_p), ("w_scale", ctypes.c_void_p),
+                ("group", ctypes.c_int), ("bias", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+def _stream_layers(layers):
+    arr = (StreamLayer * len(layers))()
+    for i, L in enumerate(layers):
+        x, wq_host, w_scale, y = L["x"], L["wq_host"], L["w_scale"], L["out"]
+        M, K = x.shape
+        N = wq_host.shape[0]
+        arr[i] = StreamLayer(_ptr(x), M, K, N, wq_host.data_ptr(), _ptr(w_scale), L["group"],
+                             _ptr(L.get("bias")), _ptr(y))
+    return arr
+
+
+def convrot_stream_slot_bytes(layers) -> int:
+    """Bytes of one weight slot for these layers (dicts as for convrot_linear_streamed)."""
+    arr = _stream_layers(layers)
+    return lib().convrot_stream_slot_bytes(arr, len(layers))
+
+
+def convrot_linear_streamed(layers, slots=None, workspace=None, copy_stream=None):
+    """Run layers whose int8 weights are in pinned host memory (see include/convrot.h).
+
+    ``layers``: list of dicts with ``x`` (bf16 CUDA [M, K]), ``wq_host`` (pinned CPU
+    int8 [N, K]), ``w_scale`` (CUDA fp32 [1]), ``group``, optional ``bias`` (bf16
+    [N]) and ``out`` (bf16 CUDA [M, N], allocated if absent).  Compute runs on the
+    current stream, the weight copies on ``copy_stream`` (a new stream if None).
+    Returns the outputs."""
+    if not layers:
+        return []
+    dev = layers[0]["x"].device
+    for L in layers:
+        _need(L["x"], torch.bfloat16, "x", 2)
+        if L["wq_host"].dtype != torch.int8 or L["wq_host"].is_cuda or not L["wq_host"].is_contiguous():
+            raise ValueError("wq_host: expected a contiguous int8 CPU tensor (pinned)")
+        if "out" not in L or L["out"] is None:
+            L["out"] = torch.empty((L["x"].shape[0], L["wq_host"].shape[0]), dtype=torch.bfloat16, device=dev)
+    arr = _stream_layers(layers)
+    slot_bytes = lib().convrot_stream_slot_bytes(arr, len(layers))
+    if slots is None:
+        slots = torch.empty(2 * slot_bytes, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        need = max(convrot_linear_workspace(L["x"].shape[0], L["x"].shape[1], L["wq_host"].shape[0])
+                   for L in layers)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if copy_stream is None:
+        copy_stream = torch.cuda.Stream(device=dev)
+    _call("convrot_linear_streamed", arr, len(layers), _ptr(slots), slots.numel() // 2, _ptr(workspace),
+          workspace.numel(), copy_stream.cuda_stream, torch.cuda.current_stream(dev).cuda_stream)
+    return [L["out"] for L in layers]

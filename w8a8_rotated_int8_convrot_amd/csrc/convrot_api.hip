@@ -274,6 +274,88 @@ int convrot_linear_ex(const void* x, int io_dtype, int64_t M, int64_t K, const i
                      workspace, ws_bytes, stream);
 }
 
+size_t convrot_stream_slot_bytes(const convrot_stream_layer* layers, int n_layers) {
+  if (!layers || n_layers < 1) return 0;
+  size_t mx = 0;
+  for (int i = 0; i < n_layers; ++i) {
+    const convrot_stream_layer& L = layers[i];
+    if (L.N > 0 && L.K > 0) {
+      const size_t b = static_cast<size_t>(L.N) * static_cast<size_t>(L.K);
+      if (b > mx) mx = b;
+    }
+  }
+  return round_up(mx, 256);
+}
+
+int convrot_linear_streamed(const convrot_stream_layer* layers, int n_layers, void* slots,
+                            size_t slot_bytes, void* workspace, size_t ws_bytes, void* copy_stream,
+                            void* stream) {
+  const char* who = "convrot_linear_streamed";
+  if (n_layers < 0 || (n_layers > 0 && !layers))
+    return fail(CONVROT_EINVAL, "%s: n_layers=%d with %s layers", who, n_layers, layers ? "non-NULL" : "NULL");
+  if (n_layers == 0) return ok();
+  if (!slots || !aligned16(slots) || slot_bytes % 16 != 0)
+    return fail(slots ? CONVROT_EALIGN : CONVROT_EINVAL, "%s: slots must be a 16-byte aligned device buffer "
+                "of 2 * slot_bytes, slot_bytes a multiple of 16", who);
+  // every layer is checked before anything is queued
+  for (int i = 0; i < n_layers; ++i) {
+    const convrot_stream_layer& L = layers[i];
+    if (int rc = check_group(L.group, L.K, who)) return rc;
+    if (int rc = check_mn(L.M, L.N, who)) return rc;
+    if (!L.wq_host || !L.w_scale || (L.M > 0 && (!L.x || !L.y)))
+      return fail(CONVROT_EINVAL, "%s: layer %d: NULL pointer", who, i);
+    if ((L.M > 0 && (!aligned16(L.x) || !aligned16(L.y))) || (workspace && !aligned16(workspace)))
+      return fail(CONVROT_EALIGN, "%s: layer %d: x, y and workspace must be 16-byte aligned", who, i);
+    if (static_cast<size_t>(L.N) * static_cast<size_t>(L.K) > slot_bytes)
+      return fail(CONVROT_EWORKSPACE, "%s: layer %d: N*K=%lld bytes exceed slot_bytes=%zu", who, i,
+                  static_cast<long long>(L.N * L.K), slot_bytes);
+    const int64_t S = workspace ? slice_rows(L.M, L.K, L.N, ws_bytes) : 0;
+    const int64_t need = L.M < 16 ? L.M : 16;
+    if (S < need)
+      return fail(CONVROT_EWORKSPACE, "%s: layer %d: workspace of %zu bytes holds %lld rows; at least %lld "
+                  "needed", who, i, ws_bytes, static_cast<long long>(S), static_cast<long long>(need));
+  }
+  for (int i = 0; i < n_layers; ++i) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, layers[i].wq_host) != hipSuccess ||
+        attr.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();   // an unregistered pointer leaves an error behind: clear it
+      return fail(CONVROT_EINVAL, "%s: layer %d: wq_host is not pinned host memory", who, i);
+    }
+  }
+
+  auto cs = static_cast<hipStream_t>(copy_stream);
+  auto s = static_cast<hipStream_t>(stream);
+  hipEvent_t ev[5] = {};   // copied[2], computed[2], start
+  for (auto& e : ev)
+    if (hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming); r != hipSuccess) {
+      for (auto& d : ev) if (d) (void)hipEventDestroy(d);
+      return hip_status(r, who);
+    }
+  hipEvent_t* copied = ev;
+  hipEvent_t* computed = ev + 2;
+  int rc = CONVROT_OK;
+  auto check = [&](hipError_t e) { if (e != hipSuccess && rc == CONVROT_OK) rc = hip_status(e, who); return e == hipSuccess; };
+  // the slots may still be read by work queued earlier on `stream`
+  if (check(hipEventRecord(ev[4], s)) && check(hipStreamWaitEvent(cs, ev[4], 0))) {
+    for (int i = 0; i < n_layers && rc == CONVROT_OK; ++i) {
+      const convrot_stream_layer& L = layers[i];
+      const int k = i & 1;
+      auto* slot = static_cast<int8_t*>(slots) + static_cast<size_t>(k) * slot_bytes;
+      if (i >= 2 && !check(hipStreamWaitEvent(cs, computed[k], 0))) break;
+      if (!check(hipMemcpyAsync(slot, L.wq_host, static_cast<size_t>(L.N) * static_cast<size_t>(L.K),
+                                hipMemcpyHostToDevice, cs))) break;
+      if (!check(hipEventRecord(copied[k], cs)) || !check(hipStreamWaitEvent(s, copied[k], 0))) break;
+      const int r = linear_impl(who, L.x, CONVROT_BF16, L.M, L.K, slot, L.w_scale, CONVROT_SCALE_TENSOR,
+                                L.N, L.group, L.bias, L.y, workspace, ws_bytes, stream);
+      if (r != CONVROT_OK) { rc = r; break; }
+      if (!check(hipEventRecord(computed[k], s))) break;
+    }
+  }
+  for (auto& e : ev) (void)hipEventDestroy(e);   // released once the queued work has passed them
+  return rc == CONVROT_OK ? ok() : rc;
+}
+
 int convrot_probe_mfma_i8(const int8_t* a, int64_t a_bytes, const int8_t* b, int64_t b_bytes,
                           int blocks, int iters, int32_t* out, void* stream) {
   const char* who = "convrot_probe_mfma_i8";
