@@ -23,6 +23,10 @@ arrays through ctypes.  The steps and their sources:
   (same page and section: the kernels run in BF16 and FP16), and one weight
   scale per output channel (page "Explanation of INT8 ConvRot", the format
   table's row-wise scaling).
+* Default path, against which the guarded layer checks its first result per
+  shape and token bucket -- page "int8 Compute", "When something goes wrong"
+  and "What stays on the default path" (such layers keep unpacking the
+  weight): the int8 weight dequantized and rotated back, times the activation.
 
 Two side outputs are computed here in float64 with numpy, not in C: the
 unquantized product ``x . W^T + bias`` (``reference_fp64``) and the NRMSE
@@ -87,7 +91,9 @@ def _load():
         lib.oracle_quant_act_ex.argtypes = [P, I, I64, I64, I, P, P, P]
         lib.oracle_epilogue_ex.argtypes = [P, P, P, I, P, I, I64, I64, P]
         lib.oracle_linear_rows_ex.argtypes = [P, I, I64, I64, P, I64, P, P, I, I64, I, P, P, P, P]
-        for name in ("oracle_hadamard", "oracle_rotate_rows", "oracle_quant_weight",
+        lib.oracle_unpack_weight.argtypes = [P, P, I, I64, I64, I, I, P]
+        lib.oracle_default_rows.argtypes = [P, I, I64, I64, P, I64, P, I64, P, P, P, P]
+        for name in ("oracle_unpack_weight", "oracle_default_rows", "oracle_hadamard", "oracle_rotate_rows", "oracle_quant_weight",
                      "oracle_quant_act", "oracle_gemm_i32", "oracle_epilogue",
                      "oracle_linear_rows", "oracle_quant_weight_rows", "oracle_quant_act_ex",
                      "oracle_epilogue_ex", "oracle_linear_rows_ex"):
@@ -279,6 +285,46 @@ def linear_rows_ex(x_bits, rows, wq, s_w, g, bias_bits=None, io: str = "bf16"):
                                          _ptr(sw), int(row), N, int(g), _ptr(bias), _ptr(y),
                                          _ptr(q), _ptr(s)), "linear_rows_ex")
     return y, q, s
+
+
+# ---------------------------------------------------------------- default path
+
+def unpack_weight(wq, s_w, g, io: str = "bf16") -> np.ndarray:
+    """The default path's unpacked weight: bf16 (or fp16) bits [N, K] of
+    rnd(O2(s_w * q)), each int8 row dequantized and rotated back (s_w: one
+    scale or one per row)."""
+    wq = np.ascontiguousarray(wq, dtype=np.int8)
+    N, K = wq.shape
+    sw = np.atleast_1d(np.ascontiguousarray(s_w, dtype=np.float32))
+    row = sw.size > 1 or (np.ndim(s_w) == 1 and N == 1)
+    if row and sw.size != N:
+        raise ValueError("unpack_weight: s_w must hold 1 or N scales")
+    wu = np.empty((N, K), dtype=np.uint16)
+    _check(_load().oracle_unpack_weight(_ptr(wq), _ptr(sw), int(row), N, K, int(g), _io(io),
+                                        _ptr(wu)), "unpack_weight")
+    return wu
+
+
+def default_rows(x_bits, rows, wu_bits, bias_bits=None, io: str = "bf16"):
+    """The default-path layer on the token rows listed.
+
+    Returns (y bits [R, N], exact float64 [R, N], mag float64 [R, N]): the
+    rounded output, the fp64 value it rounds, and sum |x * wu| + |bias|."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    wu_bits = np.ascontiguousarray(wu_bits, dtype=np.uint16)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    M, K = x_bits.shape
+    N, K2 = wu_bits.shape
+    assert K == K2
+    R = rows.shape[0]
+    bias = None if bias_bits is None else np.ascontiguousarray(bias_bits, dtype=np.uint16)
+    y = np.empty((R, N), dtype=np.uint16)
+    exact = np.empty((R, N), dtype=np.float64)
+    mag = np.empty((R, N), dtype=np.float64)
+    _check(_load().oracle_default_rows(_ptr(x_bits), _io(io), M, K, _ptr(rows), R, _ptr(wu_bits),
+                                       N, _ptr(bias), _ptr(y), _ptr(exact), _ptr(mag)),
+           "default_rows")
+    return y, exact, mag
 
 
 # ---------------------------------------------------------------- fp64 side outputs

@@ -363,3 +363,74 @@ int oracle_linear_rows_ex(const uint16_t *x, int io_f16, int64_t M, int64_t K,
     free(rot); free(q); free(acc);
     return rc;
 }
+
+/* ---------------------------------------------------------------- default path
+ *
+ * The guarded layer is checked against the default path, which keeps
+ * unpacking the weight (page "int8 Compute", InvokeAI docs, "When something
+ * goes wrong" and "What stays on the default path").  Unpacking a rotated
+ * int8 weight: dequantize each row (s_w * q in fp32) and rotate it back by R.
+ * R = blockdiag(H_g / sqrt(g)) is symmetric and orthogonal, so R^-1 = R and
+ * the same O2 butterfly undoes the rotation; the result is rounded to the
+ * compute format.  The layer is then the plain product of the (unrotated)
+ * activation with the unpacked weight, plus the bias.
+ */
+int oracle_unpack_weight(const int8_t *wq, const float *s_w, int row_scale, int64_t N,
+                         int64_t K, int g, int io_f16, uint16_t *wu)
+{
+    if (!is_pow2(g) || N < 1 || K < 1 || (K % g) != 0 || wq == NULL || s_w == NULL ||
+        wu == NULL)
+        return -1;
+    float *row = (float *)malloc((size_t)K * sizeof(float));
+    if (!row) return -3;
+    float c = oracle_rot_scale(g);
+    for (int64_t n = 0; n < N; ++n) {
+        float s = s_w[row_scale ? n : 0];
+        for (int64_t k = 0; k < K; ++k) row[k] = s * (float)wq[n * K + k];
+        for (int64_t b = 0; b < K; b += g) rotate_block(row + b, g, c);
+        for (int64_t k = 0; k < K; ++k) wu[n * K + k] = f32_to_io(row[k], io_f16);
+    }
+    free(row);
+    return 0;
+}
+
+/* y[r][n] = rnd(sum_k x[rows[r]][k] * wu[n][k] + bias[n]).  Each product of two
+ * bf16 (8-bit significand) or fp16 (11-bit) values is exact in fp64; the sum
+ * runs in fp64 in ascending k and is then rounded to fp32 and to the io
+ * format.  exact (nullable, fp64 [R, N]) receives the fp64 sum with the bias;
+ * mag (nullable, fp64 [R, N]) receives sum_k |x * wu| + |bias|, the scale of
+ * the rounding error of any fp32 evaluation of the same sum. */
+int oracle_default_rows(const uint16_t *x, int io_f16, int64_t M, int64_t K,
+                        const int64_t *rows, int64_t R, const uint16_t *wu, int64_t N,
+                        const uint16_t *bias, uint16_t *y, double *exact, double *mag)
+{
+    if (M < 1 || K < 1 || N < 1 || R < 0 || x == NULL || wu == NULL || y == NULL ||
+        (R > 0 && rows == NULL))
+        return -1;
+    for (int64_t r = 0; r < R; ++r)
+        if (rows[r] < 0 || rows[r] >= M) return -1;
+    double *xr = (double *)malloc((size_t)(R > 0 ? R : 1) * (size_t)K * sizeof(double));
+    double *wr = (double *)malloc((size_t)K * sizeof(double));
+    if (!xr || !wr) { free(xr); free(wr); return -3; }
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t k = 0; k < K; ++k) xr[r * K + k] = io_to_f32(x[rows[r] * K + k], io_f16);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) wr[k] = io_to_f32(wu[n * K + k], io_f16);
+        double b = bias ? (double)io_to_f32(bias[n], io_f16) : 0.0;
+        for (int64_t r = 0; r < R; ++r) {
+            double sum = 0.0, abs_sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double t = xr[r * K + k] * wr[k];
+                sum += t;
+                abs_sum += fabs(t);
+            }
+            sum += b;
+            abs_sum += fabs(b);
+            y[r * N + n] = f32_to_io((float)sum, io_f16);
+            if (exact) exact[r * N + n] = sum;
+            if (mag) mag[r * N + n] = abs_sum;
+        }
+    }
+    free(xr); free(wr);
+    return 0;
+}

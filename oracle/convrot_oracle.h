@@ -28,6 +28,8 @@
  *   variants: fp16 in place of bf16 for x, bias and y (IEEE binary16, RNE,
  *        overflow to infinity); one weight scale per output channel, computed
  *        like a token's (alpha = s_x[m] * s_w[n]).
+ *   default path: the weight unpacked (dequantized in fp32, rotated back by
+ *        R = R^-1, rounded to bf16/fp16), times the unrotated activation.
  *
  * All arrays are row-major and contiguous.  bf16 values travel as their raw
  * uint16 bit patterns.  Functions return 0 on success and a negative value on
@@ -116,6 +118,22 @@ int oracle_linear_rows_ex(const uint16_t *x, int io_f16, int64_t M, int64_t K,
                           const int8_t *wq, const float *s_w, int row_scale, int64_t N, int g,
                           const uint16_t *bias, uint16_t *y,
                           int8_t *q_rows, float *s_rows);
+
+/* Default path (page "int8 Compute", InvokeAI docs, "When something goes
+ * wrong": the first result of the int8 layer is checked against it; "What
+ * stays on the default path": such layers keep unpacking their weights).
+ * Unpack: wu[n] = rnd(O2(s_w[row_scale ? n : 0] * wq[n])), the dequantized
+ * row rotated back (R^-1 = R), rnd = bf16 or fp16 RNE.  wu: io bits [N, K]. */
+int oracle_unpack_weight(const int8_t *wq, const float *s_w, int row_scale, int64_t N,
+                         int64_t K, int g, int io_f16, uint16_t *wu);
+
+/* Default-path layer on the rows listed: y[r][n] = rnd(sum_k x[rows[r]][k] *
+ * wu[n][k] + bias[n]), the sum in fp64 (exact products), then fp32, then io.
+ * exact / mag (nullable, fp64 [R, N]): the fp64 sum with the bias, and
+ * sum_k |x * wu| + |bias|. */
+int oracle_default_rows(const uint16_t *x, int io_f16, int64_t M, int64_t K,
+                        const int64_t *rows, int64_t R, const uint16_t *wu, int64_t N,
+                        const uint16_t *bias, uint16_t *y, double *exact, double *mag);
 
 #ifdef __cplusplus
 }

@@ -596,3 +596,147 @@ def test_linear_variants_rows_match_full_layer():
     ref = oracle.f16_bits_to_f32(x).astype(np.float64) @ w.astype(np.float64).T \
         + oracle.f16_bits_to_f32(bias).astype(np.float64)
     assert oracle.nrmse(oracle.f16_bits_to_f32(y), ref) < 0.05
+
+
+# ---------------------------------------------------------------- default path (the guarded layer's check)
+
+def rn_bf16(q: Fraction) -> Fraction:
+    """Exact round-to-nearest-even of a rational to bf16 (8-bit significand,
+    normal range)."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (e - 7)
+    m = a / ulp
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * ulp
+
+
+def io_value(bits16: int, io: str) -> Fraction:
+    if io == "f16":
+        return f16_value(bits16)
+    return Fraction(float(oracle.bf16_bits_to_f32(np.array([bits16], np.uint16))[0]))
+
+
+def representable_weight(N, K, exps, seed):
+    """W = 2^-e_n * P H / 16 per 256-block (g = 256, where R = H / 16 exactly),
+    with integer P: max |P| = 127 in every row and sum |P| <= 256 per block, so
+    every entry of W is an integer of magnitude <= 256 times 2^-e_n / 16, exact
+    in bf16 and fp16.  Then W R = 2^-e_n P: the codes are P and each row's
+    scale is 2^-e_n (one scale 2^-e when all e_n are equal).  Returns (P, W)
+    with W in float64."""
+    g = 256
+    r = rng(seed)
+    H = oracle.hadamard(g).astype(np.int64)
+    P = np.zeros((N, K), np.int64)
+    for n in range(N):
+        for b in range(K // g):
+            idx = r.choice(g, size=5, replace=False)
+            P[n, b * g + idx] = r.integers(-30, 31, size=5)
+        P[n, r.integers(0, K)] = 127 if r.random() < 0.5 else -127
+    W = np.zeros((N, K), np.float64)
+    for n in range(N):
+        for b in range(K // g):
+            W[n, b * g:(b + 1) * g] = (H @ P[n, b * g:(b + 1) * g]) * 2.0 ** -exps[n] / 16
+    assert np.max(np.abs(W * 16 * 2.0 ** np.asarray(exps)[:, None])) <= 256
+    return P, W
+
+
+@pytest.mark.parametrize("io", ("bf16", "f16"))
+@pytest.mark.parametrize("row_scale", (False, True))
+def test_unpack_inverts_weight_preparation_exactly(io, row_scale):
+    N, K = 6, 512
+    exps = [7, 5, 9, 6, 8, 7] if row_scale else [7] * N
+    P, W = representable_weight(N, K, exps, seed=11 + row_scale)
+    w32 = W.astype(np.float32)
+    assert np.array_equal(w32.astype(np.float64), W)
+    wq, s_w = (oracle.quant_weight_rows if row_scale else oracle.quant_weight)(w32, 256)
+    assert np.array_equal(wq, P.astype(np.int8))
+    want_s = np.float32(2.0) ** -np.array(exps, np.float32)
+    assert np.array_equal(np.atleast_1d(s_w), want_s if row_scale else want_s[:1])
+    # unpacking = dequantize and rotate back: the original weight, bit for bit
+    wu = oracle.unpack_weight(wq, s_w, 256, io=io)
+    want = synth.to_bf16_bits(w32) if io == "bf16" else oracle.f32_to_f16_bits(w32)
+    assert np.array_equal(wu, want)
+    # without rotating back, the unpacked rows would be 2^-e P, not W
+    assert not np.array_equal(wu, synth.to_bf16_bits((P * want_s[:, None]).astype(np.float32)))
+
+
+@pytest.mark.parametrize("io", ("bf16", "f16"))
+def test_unpack_weight_brute_force_g128(io):
+    # g = 128: c_g is not exact; each unpacked value is the rounding of
+    # s_w * q R (explicit fp64 matrix) up to the fp32 rotation error
+    r = rng(12)
+    N, K, g = 5, 384, 128
+    wq = r.integers(-127, 128, size=(N, K)).astype(np.int8)
+    s_w = np.float32(3.1e-3)
+    wu = oracle.unpack_weight(wq, s_w, g, io=io)
+    H = oracle.hadamard(g).astype(np.float64) / np.sqrt(g)
+    R = scipy.linalg.block_diag(*([H] * (K // g)))
+    exact = (wq.astype(np.float64) * np.float64(s_w)) @ R
+    got = (oracle.bf16_bits_to_f32(wu) if io == "bf16" else oracle.f16_bits_to_f32(wu)).astype(np.float64)
+    p = 8 if io == "bf16" else 11
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact), 1e-30))) - (p - 1))
+    blocks = np.abs(wq.astype(np.float64) * s_w).reshape(N, K // g, g).sum(2).repeat(g, axis=1)
+    rot_err = (np.log2(g) + 2) * 2.0 ** -24 * blocks / np.sqrt(g)
+    assert np.all(np.abs(got - exact) <= ulp / 2 + rot_err)
+    # and almost every value is exactly the rounding of the exact one
+    near = np.abs(got - exact) <= ulp / 2 * (1 + 1e-12)
+    assert near.mean() >= 0.99
+
+
+@pytest.mark.parametrize("io", ("bf16", "f16"))
+def test_default_rows_closed_form(io):
+    N, K, M = 7, 512, 5          # N != K != M: a transposed operand cannot pass
+    P, W = representable_weight(N, K, [7] * N, seed=13)
+    wq, s_w = oracle.quant_weight(W.astype(np.float32), 256)
+    wu = oracle.unpack_weight(wq, s_w, 256, io=io)
+    r = rng(14)
+    xi = r.integers(-8, 9, size=(M, K))
+    bi = r.integers(-64, 65, size=N)
+    enc = synth.to_bf16_bits if io == "bf16" else oracle.f32_to_f16_bits
+    x = enc(xi.astype(np.float32))
+    bias = enc((bi / 16.0).astype(np.float32))
+    rows = np.array([4, 0, 2])
+    y, exact, mag = oracle.default_rows(x, rows, wu, bias, io=io)
+    Wf = [[Fraction(int(round(W[n, k] * 2 ** 11)), 2 ** 11) for k in range(K)] for n in range(N)]
+    rnd = rn_bf16 if io == "bf16" else rn_f16
+    for i, m in enumerate(rows):
+        for n in range(N):
+            val = sum(int(xi[m, k]) * Wf[n][k] for k in range(K)) + Fraction(int(bi[n]), 16)
+            assert Fraction(exact[i, n]) == val
+            assert io_value(int(y[i, n]), io) == rnd(val), (m, n)
+            assert mag[i, n] == float(sum(abs(int(xi[m, k]) * Wf[n][k]) for k in range(K))
+                                      + abs(Fraction(int(bi[n]), 16)))
+    # without a bias the outputs are the plain products
+    y0, exact0, _ = oracle.default_rows(x, rows, wu, None, io=io)
+    assert np.array_equal(exact0, exact - (bi / 16.0)[None, :])
+
+
+def test_default_path_is_the_unquantized_layer():
+    # the default path quantizes only the weight, so on outlier activations it
+    # is closer to the unquantized product than the int8 layer is
+    L = synth.make_layer("tiny")
+    ref = oracle.reference_fp64(L.x_bits, L.w, L.bias_bits)
+    wq, s_w = oracle.quant_weight(L.w, L.g)
+    wu = oracle.unpack_weight(wq, s_w, L.g)
+    rows = np.arange(L.M)
+    y_def, exact, mag = oracle.default_rows(L.x_bits, rows, wu, L.bias_bits)
+    y_int8, _, _ = oracle.linear(L.x_bits, wq, s_w, L.g, L.bias_bits)
+    e_def = oracle.nrmse(oracle.bf16_bits_to_f32(y_def), ref)
+    e_int8 = oracle.nrmse(oracle.bf16_bits_to_f32(y_int8), ref)
+    assert e_def < 0.02 and e_def < e_int8
+    # the fp64 sums against an independent fp64 matmul of the same values
+    xd = oracle.bf16_bits_to_f32(L.x_bits).astype(np.float64)
+    wd = oracle.bf16_bits_to_f32(wu).astype(np.float64)
+    alt = xd @ wd.T + oracle.bf16_bits_to_f32(L.bias_bits).astype(np.float64)[None, :]
+    assert np.all(np.abs(alt - exact) <= 1e-12 * mag)
