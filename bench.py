@@ -23,8 +23,11 @@ CPU oracle timed on a bounded sample of token rows.  Beside them:
                 fraction of it;
   paths         the HBM-bound steps against 8 TB/s: rotate+quant of this
                 workload, and the few-token layer (M=16, K=4096, N=12288)
-                with its weight read from HBM on every call; and the fp16 /
-                row-wise-scale variant of the whole layer at this shape.
+                with its weight read from HBM on every call; the fp16 /
+                row-wise-scale variant of the whole layer at this shape;
+                the default (dequantizing) path at this shape -- unpack the
+                int8 weight to bf16, then the bf16 product -- beside the
+                int8 layer; and the guarded layer once its check has run.
 """
 import argparse
 import hashlib
@@ -305,6 +308,35 @@ def main():
     torch.cuda.synchronize()
     var_ms = ev[0].elapsed_time(ev[1]) / args.steps
 
+    # the default (dequantizing) path at the same shape: the weight unpacked
+    # to bf16 on every call, then the bf16 product on the matrix cores; and
+    # the guarded int8 layer after its first (checking) call
+    ws_def = torch.empty(binding.convrot_default_workspace(K, N), dtype=torch.uint8, device=dev)
+    wu = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    ws_g = torch.empty(binding.convrot_guarded_workspace(M, K, N), dtype=torch.uint8, device=dev)
+    binding.convrot_guard_configure(0.1, log_to_stderr=False)
+    binding.convrot_guard_reset(0)
+    binding.convrot_linear_guarded(x, wq, s_w, g, bias, out=y, workspace=ws_g)   # the check
+    guard_state = binding.convrot_guard_query(0)
+
+    def timed_ms(fn, n):
+        for _ in range(3):
+            fn()
+        ev[0].record(stream)
+        for _ in range(n):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / n
+
+    def_ms = timed_ms(lambda: binding.convrot_default_linear(x, wq, s_w, g, bias, out=y, workspace=ws_def),
+                      max(args.steps // 4, 5))
+    unpack_ms = timed_ms(lambda: binding.convrot_unpack_weight(wq, s_w, g, out=wu), max(args.steps // 4, 5))
+    guarded_ms = timed_ms(lambda: binding.convrot_linear_guarded(x, wq, s_w, g, bias, out=y, workspace=ws_g),
+                          args.steps)
+    binding.convrot_guard_reset(0)
+    del ws_def, wu, ws_g
+
     ops = 2.0 * M * N * K
     value = ops / step_s / 1e12
     achieved = ops / (gemm_ms * 1e-3) / 1e12
@@ -352,6 +384,16 @@ def main():
                                 "activation, bias and output and one weight scale per output channel",
                                 "ms": round(var_ms, 5), "value": round(ops / (var_ms * 1e-3) / 1e12, 2),
                                 "unit": "TOPS"},
+        "default_path": {"entry": "convrot_default_linear", "workload": "the bench shape on the default "
+                         "path: int8 weight unpacked to bf16 (dequantized, rotated back) on every call, "
+                         "then the bf16 product with fp32 accumulation",
+                         "ms": round(def_ms, 5), "unpack_ms": round(unpack_ms, 5),
+                         "product_tflops": round(ops / ((def_ms - unpack_ms) * 1e-3) / 1e12, 1),
+                         "bf16_peak_tflops": 2500.0,
+                         "int8_layer_speedup": round(def_ms / step_ms_events, 3)},
+        "guarded": {"entry": "convrot_linear_guarded", "ms": round(guarded_ms, 5),
+                    "check_rel_error": round(guard_state["last_error"], 5),
+                    "fallback": guard_state["fallback"]},
     }
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)

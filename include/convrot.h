@@ -36,7 +36,9 @@
  *     frees or keeps a pointer after the call returns.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every launch is asynchronous on that stream; no entry point waits for
- *     the device.  Outputs are valid once the stream has reached the call.
+ *     the device, except the check that convrot_linear_guarded runs on its
+ *     first call per layer shape and token bucket.  Outputs are valid once
+ *     the stream has reached the call.
  *   - Argument errors are found before any launch and return a negative
  *     status without touching the device; convrot_last_error() then holds a
  *     message.  A failed launch returns CONVROT_EHIP.  Faults inside a kernel
@@ -231,6 +233,110 @@ size_t convrot_stream_slot_bytes(const convrot_stream_layer *layers, int n_layer
 int convrot_linear_streamed(const convrot_stream_layer *layers, int n_layers,
                             void *slots, size_t slot_bytes, void *workspace, size_t ws_bytes,
                             void *copy_stream, void *stream);
+
+/* ---------------------------------------------------------------- default path and guarded layer
+ * Page "int8 Compute" (InvokeAI docs):
+ *   - "What stays on the default path": layers outside the int8 path keep
+ *     unpacking their weights per forward.  Here the default path of a
+ *     rotated int8 weight is: dequantize each row (s * q in fp32, s the
+ *     tensor scale or the row's), rotate it back by R (R is symmetric and
+ *     orthogonal, so R^-1 = R: the same fp32 butterfly and multiply as
+ *     above), round to the compute dtype (bf16 or fp16, RNE); the layer is
+ *     then y = rnd(x . Wu^T + bias), the product in the compute dtype with an
+ *     fp32 accumulator on the bf16/fp16 matrix cores.  The activation is not
+ *     rotated or quantized.
+ *   - "When something goes wrong": the first result for each layer shape and
+ *     token-count bucket is checked against the default path; if it does not
+ *     match, or a kernel fails, one warning is logged and that GPU uses the
+ *     default path until the process ends.
+ *   - "Memory": the default path reserves the unpacked weight (2*N*K bytes);
+ *     the check keeps 256 rows of the layer's output from each path.
+ *   - "Enabling": a line is logged once per GPU when the int8 path is first
+ *     used on it.
+ */
+
+/* Bytes of workspace convrot_default_linear needs: the unpacked weight,
+ * 2*N*K rounded up to 256.  0 for a bad size. */
+size_t convrot_default_workspace(int64_t K, int64_t N);
+
+/* Unpack a rotated int8 weight (as written by convrot_prepare_weight[_ex]):
+ * wu[n][k] = rnd((W_n R)[k]) of the dequantized row W_n = s * wq[n], rnd =
+ * bf16 (out_dtype CONVROT_BF16) or fp16 (CONVROT_F16).  wq: int8 [N, K];
+ * w_scale: 1 float (CONVROT_SCALE_TENSOR) or N (CONVROT_SCALE_ROW); wu: 16-bit
+ * [N, K].  Same checks as convrot_prepare_weight_ex (group, K, N, alignment of
+ * wq and wu, dtype and scale mode). */
+int convrot_unpack_weight(const int8_t *wq, const float *w_scale, int scale_mode, int64_t N, int64_t K,
+                          int group, int out_dtype, void *wu, void *stream);
+
+/* The default path for a whole batch: unpack the weight into the workspace
+ * (convrot_default_workspace bytes), then y = rnd(x . Wu^T + bias).  Arguments
+ * as convrot_linear_ex (x, bias and y in io_dtype); the same checks. */
+int convrot_default_linear(const void *x, int io_dtype, int64_t M, int64_t K, const int8_t *wq,
+                           const float *w_scale, int scale_mode, int64_t N, int group,
+                           const void *bias, void *y, void *workspace, size_t ws_bytes,
+                           void *stream);
+
+/* Bytes of workspace convrot_linear_guarded needs: enough for
+ * convrot_linear_ex and for the check (the unpacked weight, 256 gathered
+ * activation rows, 256 default-path output rows and the per-row sums). */
+size_t convrot_guarded_workspace(int64_t M, int64_t K, int64_t N);
+
+/* The int8 layer (convrot_linear_ex), guarded.  Per device (the current HIP
+ * device), the library keeps: the set of (N, K, group, io dtype, scale mode,
+ * token bucket) already checked, where the token bucket is M rounded up to a
+ * power of two, and a sticky fallback flag.
+ *   - Fallback set: the call runs convrot_default_linear.
+ *   - Else the int8 layer runs.  If its launch fails, the fallback is set
+ *     (one warning) and the call reruns on the default path.
+ *   - On the first call for a bucket the default path is also run on
+ *     R = min(M, 256) rows spread evenly over the batch (row_i =
+ *     i * (M - 1) / (R - 1)), and the call waits for the stream to compare
+ *     them: the int8 result matches when all its R rows are finite and
+ *     ||y_int8 - y_default||_F / ||y_default||_F <= tol over those rows
+ *     (tol = 0.1 unless configured; the int8 layer differs from the default
+ *     path by its activation quantization).  A match marks the bucket
+ *     checked; a mismatch sets the fallback (one warning) and recomputes
+ *     the whole output on the default path.
+ * Argument errors return as for convrot_linear_ex and change no state.  A
+ * checking call cannot be captured into a graph: it returns
+ * CONVROT_EUNSUPPORTED if `stream` is capturing (run one call per bucket
+ * first).  Calls that need no check add no synchronisation.  Concurrent
+ * calls are safe; the state is guarded by a lock. */
+int convrot_linear_guarded(const void *x, int io_dtype, int64_t M, int64_t K, const int8_t *wq,
+                           const float *w_scale, int scale_mode, int64_t N, int group,
+                           const void *bias, void *y, void *workspace, size_t ws_bytes,
+                           void *stream);
+
+/* Guard state of one device, for logs and tests. */
+typedef struct convrot_guard_info {
+    int     fallback;       /* 1: this device runs the default path */
+    int64_t checked;        /* buckets checked and matched */
+    int64_t checks_run;     /* checks run (matched or not) */
+    double  last_error;     /* relative error of the latest check; -1 if none */
+    char    message[256];   /* the latest log line for this device, "" if none */
+} convrot_guard_info;
+
+/* Host pointer info.  CONVROT_EINVAL for a NULL pointer or a negative device. */
+int convrot_guard_query(int device, convrot_guard_info *info);
+
+/* Forget the state of one device (checked buckets, fallback, pending
+ * injection).  CONVROT_EINVAL for a negative device. */
+int convrot_guard_reset(int device);
+
+/* Match tolerance (finite, > 0) and whether log lines also go to stderr
+ * (they are always kept in convrot_guard_info.message).  Applies to every
+ * device.  CONVROT_EINVAL for a bad tolerance. */
+int convrot_guard_configure(double tol, int log_to_stderr);
+
+/* Fault injection from the host, for tests of the guard: arms one fault on
+ * a device, consumed by the next convrot_linear_guarded call there that runs
+ * the int8 layer.  CONVROT_FAULT_MISMATCH makes that call's check see the
+ * int8 rows negated (and runs the check even if the bucket was checked);
+ * CONVROT_FAULT_KERNEL makes the int8 launch report a failure.  Nothing is
+ * done to the GPU.  CONVROT_EINVAL for an unknown fault or a negative
+ * device. */
+enum convrot_fault { CONVROT_FAULT_NONE = 0, CONVROT_FAULT_MISMATCH = 1, CONVROT_FAULT_KERNEL = 2 };
+int convrot_guard_inject(int device, int fault);
 
 /* ---------------------------------------------------------------- measurement aid
  * Not a step of the layer and defined by no page: it exists so that a

@@ -184,3 +184,63 @@ def test_streamed_argument_errors(lib, binding):
     assert f(bad, 1, A, 1 << 16, A, 1 << 20, None, None) == EUNSUPPORTED       # group
     assert lib.convrot_stream_slot_bytes(arr, 2) == 64 * 512
     assert ctypes.sizeof(binding.StreamLayer) == 72
+
+
+def test_default_path_and_guard_argument_errors(lib):
+    F16, BF16 = 2, 1
+    big = 1 << 30
+    # default path: the layer rules, and a workspace of at least the unpacked weight
+    assert lib.convrot_default_workspace(512, 64) == 2 * 512 * 64
+    assert lib.convrot_default_linear(A, BF16, 64, 512, A, A, 0, 64, 128, None, A, A, 2 * 512 * 64 - 1,
+                                      None) == EWORKSPACE
+    assert lib.convrot_default_linear(A, BF16, 64, 500, A, A, 0, 64, 128, None, A, A, big, None) == EINVAL
+    assert lib.convrot_default_linear(A, BF16, 64, 512, A, A, 0, 64, 96, None, A, A, big, None) == EUNSUPPORTED
+    assert lib.convrot_default_linear(A, 0, 64, 512, A, A, 0, 64, 128, None, A, A, big, None) == EUNSUPPORTED
+    assert lib.convrot_default_linear(A + 2, F16, 64, 512, A, A, 0, 64, 128, None, A, A, big, None) == EALIGN
+    assert lib.convrot_default_linear(None, BF16, 0, 512, None, None, 0, 64, 128, None, None, None, 0,
+                                      None) == OK
+    assert lib.convrot_unpack_weight(A, A, 0, 64, 512, 128, 0, A, None) == EUNSUPPORTED   # fp32 out
+    assert lib.convrot_unpack_weight(A, A, 2, 64, 512, 128, BF16, A, None) == EUNSUPPORTED
+    assert lib.convrot_unpack_weight(A, None, 0, 64, 512, 128, BF16, A, None) == EINVAL
+    assert lib.convrot_unpack_weight(A, A, 0, 64, 512, 128, BF16, A + 8, None) == EALIGN
+    # guarded layer: the same rules, and its own workspace
+    ws = lib.convrot_guarded_workspace(64, 512, 64)
+    assert lib.convrot_linear_guarded(A, BF16, 64, 512, A, A, 0, 64, 128, None, A, A, ws - 1, None) == EWORKSPACE
+    assert lib.convrot_linear_guarded(A, BF16, 64, 512, A, A, 3, 64, 128, None, A, A, ws, None) == EUNSUPPORTED
+    assert lib.convrot_linear_guarded(A, BF16, 64, 512, A, A, 0, 0, 128, None, A, A, ws, None) == EINVAL
+    assert lib.convrot_linear_guarded(None, BF16, 0, 512, None, None, 0, 64, 128, None, None, None, 0,
+                                      None) == OK
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 1), (300, 512, 64), (4608, 3072, 12288), (16, 4096, 12288)])
+def test_guarded_workspace_is_the_unpacked_weight_plus_the_kept_rows(lib, M, K, N):
+    # page "int8 Compute", "Memory": the default path reserves the unpacked
+    # weight; the check keeps 256 rows of the output from each path (here also
+    # the 256 gathered activation rows and three fp64 sums per row)
+    R = min(M, 256)
+    pad = lambda v: (v + 255) // 256 * 256
+    ws = lib.convrot_guarded_workspace(M, K, N)
+    assert ws >= lib.convrot_linear_workspace(M, K, N)
+    assert ws == max(lib.convrot_linear_workspace(M, K, N),
+                     pad(2 * N * K) + pad(2 * R * K) + pad(2 * R * N) + pad(24 * R))
+
+
+def test_guard_state_on_the_host(lib, binding):
+    # state functions touch no device
+    binding.convrot_guard_reset(5)
+    st = binding.convrot_guard_query(5)
+    assert st == {"fallback": False, "checked": 0, "checks_run": 0, "last_error": -1.0, "message": ""}
+    binding.convrot_guard_inject(5, "mismatch")
+    binding.convrot_guard_inject(5, "none")
+    binding.convrot_guard_reset(5)
+    assert lib.convrot_guard_inject(5, 9) == EINVAL
+    assert lib.convrot_guard_inject(-1, 1) == EINVAL
+    assert lib.convrot_guard_query(0, None) == EINVAL
+    assert lib.convrot_guard_reset(-2) == EINVAL
+    assert lib.convrot_guard_configure(0.0, 1) == EINVAL
+    assert lib.convrot_guard_configure(float("nan"), 1) == EINVAL
+    assert lib.convrot_guard_configure(float("inf"), 1) == EINVAL
+    assert lib.convrot_guard_configure(0.1, 1) == OK
+    with pytest.raises(ValueError):
+        binding.convrot_guard_inject(0, "segfault")
+    assert ctypes.sizeof(binding.GuardInfo) == 288

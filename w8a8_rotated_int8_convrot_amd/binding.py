@@ -44,7 +44,20 @@ SIGNATURES = {
     "convrot_linear_ex": ([_P, _I, _I64, _I64, _P, _P, _I, _I64, _I, _P, _P, _P, _SZ, _P], _I),
     "convrot_stream_slot_bytes": ([_P, _I], _SZ),
     "convrot_linear_streamed": ([_P, _I, _P, _SZ, _P, _SZ, _P, _P], _I),
+    "convrot_default_workspace": ([_I64, _I64], _SZ),
+    "convrot_unpack_weight": ([_P, _P, _I, _I64, _I64, _I, _I, _P, _P], _I),
+    "convrot_default_linear": ([_P, _I, _I64, _I64, _P, _P, _I, _I64, _I, _P, _P, _P, _SZ, _P], _I),
+    "convrot_guarded_workspace": ([_I64, _I64, _I64], _SZ),
+    "convrot_linear_guarded": ([_P, _I, _I64, _I64, _P, _P, _I, _I64, _I, _P, _P, _P, _SZ, _P], _I),
+    "convrot_guard_query": ([_I, _P], _I),
+    "convrot_guard_reset": ([_I], _I),
+    "convrot_guard_configure": ([ctypes.c_double, _I], _I),
+    "convrot_guard_inject": ([_I, _I], _I),
 }
+
+CONVROT_FAULT_NONE = 0
+CONVROT_FAULT_MISMATCH = 1
+CONVROT_FAULT_KERNEL = 2
 
 
 class ConvrotError(RuntimeError):
@@ -390,3 +403,103 @@ def convrot_linear_streamed(layers, slots=None, workspace=None, copy_stream=None
     _call("convrot_linear_streamed", arr, len(layers), _ptr(slots), slots.numel() // 2, _ptr(workspace),
           workspace.numel(), copy_stream.cuda_stream, torch.cuda.current_stream(dev).cuda_stream)
     return [L["out"] for L in layers]
+
+
+# ---------------------------------------------------------------- default path and guarded layer
+
+def convrot_default_workspace(K: int, N: int) -> int:
+    return lib().convrot_default_workspace(K, N)
+
+
+def convrot_guarded_workspace(M: int, K: int, N: int) -> int:
+    return lib().convrot_guarded_workspace(M, K, N)
+
+
+def convrot_unpack_weight(wq, w_scale, group, out_dtype=torch.bfloat16, out=None) -> torch.Tensor:
+    """int8 codes [N, K] and 1 or N scales -> the unpacked weight [N, K] in bf16 or fp16."""
+    _need(wq, torch.int8, "wq", 2)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    N, K = wq.shape
+    mode = _scale_mode_of(w_scale, N, "convrot_unpack_weight")
+    wu = torch.empty((N, K), dtype=out_dtype, device=wq.device) if out is None else out
+    io = _io_of(wu, "out")
+    _need(wu, wu.dtype, "out", 2)
+    if tuple(wu.shape) != (N, K):
+        raise ValueError("convrot_unpack_weight: output shape mismatch")
+    _call("convrot_unpack_weight", _ptr(wq), _ptr(w_scale), mode, N, K, group, io, _ptr(wu), _stream(wq))
+    return wu
+
+
+def _layer_args(who, x, wq, w_scale, bias, out):
+    io = _io_of(x, "x")
+    _need(x, x.dtype, "x", 2)
+    _need(wq, torch.int8, "wq", 2)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError(f"{who}: K mismatch")
+    mode = _scale_mode_of(w_scale, N, who)
+    if bias is not None:
+        _need(bias, x.dtype, "bias", 1)
+        if bias.numel() != N:
+            raise ValueError(f"{who}: bias must have N elements")
+    y = torch.empty((M, N), dtype=x.dtype, device=x.device) if out is None else out
+    _need(y, x.dtype, "out", 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError(f"{who}: output shape mismatch")
+    return io, M, K, N, mode, y
+
+
+def convrot_default_linear(x, wq, w_scale, group, bias=None, out=None, workspace=None) -> torch.Tensor:
+    """The default (dequantizing) path: unpack the weight, y = x . Wu^T + bias in
+    x's dtype (bf16 or fp16) with fp32 accumulation."""
+    io, M, K, N, mode, y = _layer_args("convrot_default_linear", x, wq, w_scale, bias, out)
+    if workspace is None:
+        workspace = torch.empty(max(convrot_default_workspace(K, N), 1), dtype=torch.uint8, device=x.device)
+    _need(workspace, torch.uint8, "workspace")
+    _call("convrot_default_linear", _ptr(x), io, M, K, _ptr(wq), _ptr(w_scale), mode, N, group, _ptr(bias),
+          _ptr(y), _ptr(workspace), workspace.numel(), _stream(x))
+    return y
+
+
+def convrot_linear_guarded(x, wq, w_scale, group, bias=None, out=None, workspace=None) -> torch.Tensor:
+    """The int8 layer, checked against the default path on its first call per
+    layer shape and token bucket, with a sticky per-device fallback."""
+    io, M, K, N, mode, y = _layer_args("convrot_linear_guarded", x, wq, w_scale, bias, out)
+    if workspace is None:
+        workspace = torch.empty(max(convrot_guarded_workspace(M, K, N), 1), dtype=torch.uint8,
+                                device=x.device)
+    _need(workspace, torch.uint8, "workspace")
+    _call("convrot_linear_guarded", _ptr(x), io, M, K, _ptr(wq), _ptr(w_scale), mode, N, group, _ptr(bias),
+          _ptr(y), _ptr(workspace), workspace.numel(), _stream(x))
+    return y
+
+
+class GuardInfo(ctypes.Structure):
+    """Mirror of ``convrot_guard_info`` (include/convrot.h)."""
+    _fields_ = [("fallback", ctypes.c_int), ("checked", ctypes.c_int64), ("checks_run", ctypes.c_int64),
+                ("last_error", ctypes.c_double), ("message", ctypes.c_char * 256)]
+
+
+def convrot_guard_query(device: int = 0) -> dict:
+    info = GuardInfo()
+    _call("convrot_guard_query", device, ctypes.byref(info))
+    return {"fallback": bool(info.fallback), "checked": info.checked, "checks_run": info.checks_run,
+            "last_error": info.last_error, "message": info.message.decode()}
+
+
+def convrot_guard_reset(device: int = 0) -> None:
+    _call("convrot_guard_reset", device)
+
+
+def convrot_guard_configure(tol: float = 0.1, log_to_stderr: bool = True) -> None:
+    _call("convrot_guard_configure", float(tol), 1 if log_to_stderr else 0)
+
+
+def convrot_guard_inject(device: int, fault: str) -> None:
+    """Arm one host-side fault ("none", "mismatch" or "kernel") for the next guarded call."""
+    codes = {"none": CONVROT_FAULT_NONE, "mismatch": CONVROT_FAULT_MISMATCH, "kernel": CONVROT_FAULT_KERNEL}
+    if fault not in codes:
+        raise ValueError("convrot_guard_inject: fault is 'none', 'mismatch' or 'kernel'")
+    _call("convrot_guard_inject", device, codes[fault])

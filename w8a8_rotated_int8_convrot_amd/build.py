@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libconvrot.so")
-SOURCES = ("convrot_api.hip", "rotate_quant.hip", "gemm_i8.hip", "mfma_probe.hip")
+SOURCES = ("convrot_api.hip", "rotate_quant.hip", "gemm_i8.hip", "default_path.hip", "mfma_probe.hip")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

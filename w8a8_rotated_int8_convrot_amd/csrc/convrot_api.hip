@@ -1,10 +1,20 @@
 // convrot_api.hip -- the C ABI declared in include/convrot.h: argument checks,
 // workspace carving, M-slicing and kernel dispatch.  No entry point allocates
-// device memory, synchronises the device or falls back to another path.
+// device memory or falls back to another path on its own; only the guarded
+// layer switches to the default path, by the rules stated in the header, and
+// only its checking calls synchronise (with their stream).
 #include "../../include/convrot.h"
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <set>
+#include <string>
+#include <tuple>
+#include <vector>
 
 #include "convrot_internal.hpp"
 
@@ -355,6 +365,304 @@ int convrot_linear_streamed(const convrot_stream_layer* layers, int n_layers, vo
   for (auto& e : ev) (void)hipEventDestroy(e);   // released once the queued work has passed them
   return rc == CONVROT_OK ? ok() : rc;
 }
+
+// ---------------------------------------------------------------- default path and guarded layer
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kCheckRows = 256;
+
+size_t default_ws(int64_t K, int64_t N) {
+  return round_up(2 * static_cast<size_t>(N) * static_cast<size_t>(K), 256);
+}
+
+// Workspace of a checking call: the unpacked weight, the gathered activation
+// rows, the default path's output rows and the per-row sums.
+struct CheckLayout {
+  int R;
+  size_t xs, ydef, partial, total;
+};
+CheckLayout check_layout(int64_t M, int64_t K, int64_t N) {
+  CheckLayout L;
+  L.R = static_cast<int>(M < kCheckRows ? M : kCheckRows);
+  const size_t R = static_cast<size_t>(L.R);
+  L.xs = default_ws(K, N);
+  L.ydef = L.xs + round_up(2 * R * static_cast<size_t>(K), 256);
+  L.partial = L.ydef + round_up(2 * R * static_cast<size_t>(N), 256);
+  L.total = L.partial + round_up(3 * sizeof(double) * R, 256);
+  return L;
+}
+
+int unpack_impl(const char* who, const int8_t* wq, const float* w_scale, int scale_mode, int64_t N,
+                int64_t K, int group, int out_dtype, void* wu, void* stream) {
+  if (int rc = check_group(group, K, who)) return rc;
+  if (int rc = check_scale_mode(scale_mode, who)) return rc;
+  if (int rc = check_io(out_dtype, who)) return rc;
+  if (N < 1 || N > (int64_t(1) << 31) - 1)
+    return fail(CONVROT_EINVAL, "%s: N=%lld must be in [1, 2^31)", who, static_cast<long long>(N));
+  if (!wq || !w_scale || !wu) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
+  if (!aligned16(wq) || !aligned16(wu)) return fail(CONVROT_EALIGN, "%s: wq and wu must be 16-byte aligned", who);
+  return hip_status(convrot::launch_unpack_weight(wq, w_scale, scale_mode == CONVROT_SCALE_ROW, N, K, group,
+                                                  out_dtype == CONVROT_F16, static_cast<uint16_t*>(wu),
+                                                  static_cast<hipStream_t>(stream)),
+                    who);
+}
+
+// Checks shared by the default path and the guarded layer (those of
+// convrot_linear_ex except the workspace).
+int check_layer(const char* who, const void* x, int io_dtype, int64_t M, int64_t K, const int8_t* wq,
+                const float* w_scale, int scale_mode, int64_t N, int group, void* y, void* workspace) {
+  if (int rc = check_group(group, K, who)) return rc;
+  if (int rc = check_mn(M, N, who)) return rc;
+  if (int rc = check_io(io_dtype, who)) return rc;
+  if (int rc = check_scale_mode(scale_mode, who)) return rc;
+  if (M == 0) return CONVROT_OK;
+  if (!x || !wq || !w_scale || !y) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(y) || (workspace && !aligned16(workspace)))
+    return fail(CONVROT_EALIGN, "%s: x, wq, y and workspace must be 16-byte aligned", who);
+  return CONVROT_OK;
+}
+
+int default_impl(const char* who, const void* x, int io_dtype, int64_t M, int64_t K, const int8_t* wq,
+                 const float* w_scale, int scale_mode, int64_t N, int group, const void* bias, void* y,
+                 void* workspace, size_t ws_bytes, void* stream) {
+  if (int rc = check_layer(who, x, io_dtype, M, K, wq, w_scale, scale_mode, N, group, y, workspace)) return rc;
+  if (M == 0) return ok();
+  if (!workspace || ws_bytes < default_ws(K, N))
+    return fail(CONVROT_EWORKSPACE, "%s: workspace of %zu bytes needed (the unpacked weight)", who,
+                default_ws(K, N));
+  auto s = static_cast<hipStream_t>(stream);
+  const bool f16 = io_dtype == CONVROT_F16;
+  auto* wu = static_cast<uint16_t*>(workspace);
+  hipError_t e = convrot::launch_unpack_weight(wq, w_scale, scale_mode == CONVROT_SCALE_ROW, N, K, group, f16,
+                                               wu, s);
+  if (e != hipSuccess) return hip_status(e, who);
+  e = convrot::launch_gemm_default(static_cast<const uint16_t*>(x), wu, static_cast<const uint16_t*>(bias),
+                                   static_cast<uint16_t*>(y), f16, M, N, K, s);
+  return hip_status(e, who);
+}
+
+// ---- guard state, per device
+struct GuardKey {
+  int64_t N, K;
+  int group, io, mode;
+  int64_t bucket;
+  bool operator<(const GuardKey& o) const {
+    return std::tie(N, K, group, io, mode, bucket) < std::tie(o.N, o.K, o.group, o.io, o.mode, o.bucket);
+  }
+};
+
+struct GuardState {
+  bool fallback = false;
+  bool announced = false;
+  std::set<GuardKey> checked;
+  int64_t checks_run = 0;
+  double last_error = -1.0;
+  int inject = CONVROT_FAULT_NONE;
+  std::string message;
+};
+
+std::mutex g_guard_mu;
+std::map<int, GuardState> g_guard;
+double g_guard_tol = 0.1;
+bool g_guard_log = true;
+
+// Called with g_guard_mu held.
+void guard_log(GuardState& st, const char* fmt, ...) {
+  char buf[256];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  st.message = buf;
+  if (g_guard_log) fprintf(stderr, "%s\n", buf);
+}
+
+void guard_fall_back(int dev, const char* why) {
+  std::lock_guard<std::mutex> lock(g_guard_mu);
+  GuardState& st = g_guard[dev];
+  if (!st.fallback) {
+    st.fallback = true;
+    guard_log(st, "convrot: %s on device %d; this device uses the default path until the process ends", why,
+              dev);
+  }
+}
+
+int64_t token_bucket(int64_t M) {
+  int64_t b = 1;
+  while (b < M) b <<= 1;
+  return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t convrot_default_workspace(int64_t K, int64_t N) {
+  if (K < 1 || N < 1) return 0;
+  return default_ws(K, N);
+}
+
+int convrot_unpack_weight(const int8_t* wq, const float* w_scale, int scale_mode, int64_t N, int64_t K,
+                          int group, int out_dtype, void* wu, void* stream) {
+  return unpack_impl("convrot_unpack_weight", wq, w_scale, scale_mode, N, K, group, out_dtype, wu, stream);
+}
+
+int convrot_default_linear(const void* x, int io_dtype, int64_t M, int64_t K, const int8_t* wq,
+                           const float* w_scale, int scale_mode, int64_t N, int group, const void* bias,
+                           void* y, void* workspace, size_t ws_bytes, void* stream) {
+  return default_impl("convrot_default_linear", x, io_dtype, M, K, wq, w_scale, scale_mode, N, group, bias, y,
+                      workspace, ws_bytes, stream);
+}
+
+size_t convrot_guarded_workspace(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || K < 1 || N < 1) return 0;
+  const size_t a = convrot_linear_workspace(M, K, N);
+  const size_t b = check_layout(M, K, N).total;
+  return a > b ? a : b;
+}
+
+int convrot_linear_guarded(const void* x, int io_dtype, int64_t M, int64_t K, const int8_t* wq,
+                           const float* w_scale, int scale_mode, int64_t N, int group, const void* bias,
+                           void* y, void* workspace, size_t ws_bytes, void* stream) {
+  const char* who = "convrot_linear_guarded";
+  if (int rc = check_layer(who, x, io_dtype, M, K, wq, w_scale, scale_mode, N, group, y, workspace)) return rc;
+  if (M == 0) return ok();
+  if (!workspace || ws_bytes < convrot_guarded_workspace(M, K, N))
+    return fail(CONVROT_EWORKSPACE, "%s: workspace of %zu bytes needed (convrot_guarded_workspace)", who,
+                convrot_guarded_workspace(M, K, N));
+  auto s = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return hip_status(e, who);
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipError_t e = hipStreamIsCapturing(s, &capture); e != hipSuccess) return hip_status(e, who);
+  const GuardKey key{N, K, group, io_dtype, scale_mode, token_bucket(M)};
+
+  bool fallback = false, need_check = false;
+  int inject = CONVROT_FAULT_NONE;
+  {
+    std::lock_guard<std::mutex> lock(g_guard_mu);
+    GuardState& st = g_guard[dev];
+    fallback = st.fallback;
+    if (!fallback) {
+      need_check = st.checked.count(key) == 0 || st.inject == CONVROT_FAULT_MISMATCH;
+      if (need_check && capture != hipStreamCaptureStatusNone)
+        return fail(CONVROT_EUNSUPPORTED, "%s: the first call for this layer shape and token bucket checks its "
+                    "result and cannot be captured; run it once before capturing", who);
+      inject = st.inject;
+      st.inject = CONVROT_FAULT_NONE;
+      if (!st.announced) {
+        st.announced = true;
+        guard_log(st, "convrot: rotated int8 layers on device %d run on the int8 matrix cores", dev);
+      }
+    }
+  }
+  if (fallback)
+    return default_impl(who, x, io_dtype, M, K, wq, w_scale, scale_mode, N, group, bias, y, workspace,
+                        ws_bytes, stream);
+
+  int rc = inject == CONVROT_FAULT_KERNEL
+               ? fail(CONVROT_EHIP, "%s: injected kernel failure", who)
+               : linear_impl(who, x, io_dtype, M, K, wq, w_scale, scale_mode, N, group, bias, y, workspace,
+                             ws_bytes, stream);
+  if (rc == CONVROT_EHIP) {
+    std::string why = std::string("the int8 layer failed (") + g_last_error + ")";
+    guard_fall_back(dev, why.c_str());
+    return default_impl(who, x, io_dtype, M, K, wq, w_scale, scale_mode, N, group, bias, y, workspace,
+                        ws_bytes, stream);
+  }
+  if (rc != CONVROT_OK || !need_check) return rc;
+
+  // the check: the default path on R rows spread over the batch
+  const CheckLayout L = check_layout(M, K, N);
+  char* ws = static_cast<char*>(workspace);
+  auto* wu = reinterpret_cast<uint16_t*>(ws);
+  auto* xs = reinterpret_cast<uint16_t*>(ws + L.xs);
+  auto* ydef = reinterpret_cast<uint16_t*>(ws + L.ydef);
+  auto* partial = reinterpret_cast<double*>(ws + L.partial);
+  const bool f16 = io_dtype == CONVROT_F16;
+  hipError_t e = convrot::launch_unpack_weight(wq, w_scale, scale_mode == CONVROT_SCALE_ROW, N, K, group, f16,
+                                               wu, s);
+  if (e == hipSuccess) e = convrot::launch_gather_rows(static_cast<const uint16_t*>(x), M, K, L.R, xs, s);
+  if (e == hipSuccess)
+    e = convrot::launch_gemm_default(xs, wu, static_cast<const uint16_t*>(bias), ydef, f16, L.R, N, K, s);
+  if (e == hipSuccess)
+    e = convrot::launch_compare_rows(static_cast<const uint16_t*>(y), ydef, f16, M, N, L.R,
+                                     inject == CONVROT_FAULT_MISMATCH, partial, s);
+  std::vector<double> host(3 * static_cast<size_t>(L.R));
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(host.data(), partial, host.size() * sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, who);
+  double d2 = 0.0, r2 = 0.0, bad = 0.0;
+  for (int i = 0; i < L.R; ++i) {
+    d2 += host[3 * i];
+    r2 += host[3 * i + 1];
+    bad += host[3 * i + 2];
+  }
+  const double rel = r2 > 0.0 ? std::sqrt(d2 / r2) : std::sqrt(d2);
+  bool match;
+  {
+    std::lock_guard<std::mutex> lock(g_guard_mu);
+    GuardState& st = g_guard[dev];
+    match = bad == 0.0 && rel <= g_guard_tol;
+    st.checks_run += 1;
+    st.last_error = rel;
+    if (match) st.checked.insert(key);
+  }
+  if (match) return ok();
+  char why[160];
+  snprintf(why, sizeof why, "the int8 result for N=%lld K=%lld, up to %lld tokens, does not match the default "
+           "path (relative error %.3g, %.0f non-finite values)", static_cast<long long>(N),
+           static_cast<long long>(K), static_cast<long long>(key.bucket), rel, bad);
+  guard_fall_back(dev, why);
+  return default_impl(who, x, io_dtype, M, K, wq, w_scale, scale_mode, N, group, bias, y, workspace, ws_bytes,
+                      stream);
+}
+
+int convrot_guard_query(int device, convrot_guard_info* info) {
+  if (device < 0 || !info) return fail(CONVROT_EINVAL, "convrot_guard_query: device %d, info %p", device,
+                                       static_cast<void*>(info));
+  std::lock_guard<std::mutex> lock(g_guard_mu);
+  GuardState st;
+  auto it = g_guard.find(device);
+  if (it != g_guard.end()) st = it->second;
+  info->fallback = st.fallback ? 1 : 0;
+  info->checked = static_cast<int64_t>(st.checked.size());
+  info->checks_run = st.checks_run;
+  info->last_error = st.last_error;
+  snprintf(info->message, sizeof info->message, "%s", st.message.c_str());
+  return ok();
+}
+
+int convrot_guard_reset(int device) {
+  if (device < 0) return fail(CONVROT_EINVAL, "convrot_guard_reset: device %d", device);
+  std::lock_guard<std::mutex> lock(g_guard_mu);
+  g_guard.erase(device);
+  return ok();
+}
+
+int convrot_guard_configure(double tol, int log_to_stderr) {
+  if (!(tol > 0.0) || !std::isfinite(tol))
+    return fail(CONVROT_EINVAL, "convrot_guard_configure: tolerance %g must be finite and > 0", tol);
+  std::lock_guard<std::mutex> lock(g_guard_mu);
+  g_guard_tol = tol;
+  g_guard_log = log_to_stderr != 0;
+  return ok();
+}
+
+int convrot_guard_inject(int device, int fault) {
+  if (device < 0 || (fault != CONVROT_FAULT_NONE && fault != CONVROT_FAULT_MISMATCH &&
+                     fault != CONVROT_FAULT_KERNEL))
+    return fail(CONVROT_EINVAL, "convrot_guard_inject: device %d, fault %d", device, fault);
+  std::lock_guard<std::mutex> lock(g_guard_mu);
+  g_guard[device].inject = fault;
+  return ok();
+}
+
+// ---------------------------------------------------------------- measurement aid
 
 int convrot_probe_mfma_i8(const int8_t* a, int64_t a_bytes, const int8_t* b, int64_t b_bytes,
                           int blocks, int iters, int32_t* out, void* stream) {

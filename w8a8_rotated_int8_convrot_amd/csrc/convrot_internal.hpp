@@ -33,6 +33,11 @@ hipError_t launch_prepare_weight(const void* w, int in_dtype, bool row_scale, in
                                  int group, int8_t* wq, float* w_scale, uint32_t* amax_cell,
                                  hipStream_t stream);
 
+// Default path: unpack a rotated int8 weight, out[n] = rnd(rotate(s * wq[n]))
+// (s = w_scale[row_scale ? n : 0]), rnd = bf16 or fp16 (out_f16) RNE.
+hipError_t launch_unpack_weight(const int8_t* wq, const float* w_scale, bool row_scale, int64_t N,
+                                int64_t K, int group, bool out_f16, uint16_t* out, hipStream_t stream);
+
 // ---------------------------------------------------------------- GEMM
 
 // GEMM + fused dequant/bias epilogue: y[m][n] (bf16) from xq [M, K] and
@@ -51,6 +56,26 @@ hipError_t launch_gemm_dequant_ex(const int8_t* xq, const float* x_scale, const 
 // Same main loop with the raw int32 products stored.
 hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// Default path product: y = rnd(x . wu^T + bias) on bf16 (or fp16, f16)
+// operands x [M, K] and wu [N, K] with an fp32 accumulator.  K % 64 == 0.
+hipError_t launch_gemm_default(const uint16_t* x, const uint16_t* wu, const uint16_t* bias, uint16_t* y,
+                               bool f16, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// ---------------------------------------------------------------- guard check
+// (default_path.hip)
+
+// xs[i] = x[row_i] for the R sampled rows row_i = i * (M - 1) / (R - 1).
+hipError_t launch_gather_rows(const uint16_t* x, int64_t M, int64_t K, int R, uint16_t* xs,
+                              hipStream_t stream);
+// Per sampled row i: partial[3i..3i+2] = {sum_n (a - b)^2, sum_n b^2, count of
+// non-finite a}, a = y[row_i][n] (negated when flip), b = ydef[i][n], in fp64.
+hipError_t launch_compare_rows(const uint16_t* y, const uint16_t* ydef, bool f16, int64_t M, int64_t N,
+                               int R, bool flip, double* partial, hipStream_t stream);
+// The sampled row i of R over M rows.
+__host__ __device__ inline int64_t sample_row(int i, int R, int64_t M) {
+  return R > 1 ? static_cast<int64_t>(i) * (M - 1) / (R - 1) : 0;
+}
 
 // ---------------------------------------------------------------- measurement aid
 

@@ -44,6 +44,13 @@
 //    tiles of one XCD share weight and activation rows in its L2.
 //  * Ragged edges: rows past M or N are loaded from the last valid row (the
 //    results are discarded) and stores are masked; K is a multiple of 128.
+//  * The same kernel runs the default (dequantizing) path's bf16 or fp16
+//    product (page "int8 Compute", "When something goes wrong": the guarded
+//    layer checks its first result against that path and may fall back to
+//    it): a v_mfma_f32_32x32x16_bf16 / _f16 lane takes 8 values = 16 bytes of
+//    one row, exactly as an int8 lane takes 16 codes, and the 32x32 result
+//    layout is the same, so the tiles are used with K counted in bytes and
+//    an fp32 accumulator; the epilogue is rnd(acc + bias).
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -145,14 +152,35 @@ __device__ inline int swz(int r) {
   else return (r >> 2) & 3;
 }
 
-template <int MF> struct Acc;
-template <> struct Acc<16> { using type = v4i; };
-template <> struct Acc<32> { using type = v16i; };
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-template <int MF>
-__device__ inline typename Acc<MF>::type mfma(v4i a, v4i b, typename Acc<MF>::type c) {
-  if constexpr (MF == 16) return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-  else return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+// Operand kinds: int8 codes (int32 accumulator) or the default path's bf16 /
+// fp16 values (fp32 accumulator).  Each lane supplies 16 bytes per MFMA.
+enum Op { kOpI8 = 0, kOpBf16 = 1, kOpF16 = 2 };
+
+template <int MF, int OP> struct Acc;
+template <> struct Acc<16, kOpI8> { using type = v4i; };
+template <> struct Acc<32, kOpI8> { using type = v16i; };
+template <int OP> struct Acc<16, OP> { using type = v4f; };
+template <int OP> struct Acc<32, OP> { using type = v16f; };
+
+template <int MF, int OP>
+__device__ inline typename Acc<MF, OP>::type mfma(v4i a, v4i b, typename Acc<MF, OP>::type c) {
+  if constexpr (OP == kOpI8) {
+    if constexpr (MF == 16) return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+  } else if constexpr (OP == kOpBf16) {
+    const v8bf a8 = __builtin_bit_cast(v8bf, a), b8 = __builtin_bit_cast(v8bf, b);
+    if constexpr (MF == 16) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, b8, c, 0, 0, 0);
+  } else {
+    const v8h a8 = __builtin_bit_cast(v8h, a), b8 = __builtin_bit_cast(v8h, b);
+    if constexpr (MF == 16) return __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, b8, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, b8, c, 0, 0, 0);
+  }
 }
 
 // s_waitcnt vmcnt(N) + s_barrier.  lgkmcnt(0) too, so that this wave's LDS
@@ -204,8 +232,10 @@ __device__ inline int out_lds_offset(int m, int n) {
 }
 
 // Epilogue modes: raw int32 products, or dequant + bias to bf16 / fp16 with
-// one weight scale (tensorwise) or one per output channel (row-wise).
-enum Epi { kEpiI32 = 0, kEpiBf16 = 1, kEpiBf16Row = 2, kEpiF16 = 3, kEpiF16Row = 4 };
+// one weight scale (tensorwise) or one per output channel (row-wise); or the
+// default path's bf16 / fp16 product with the bias added (no scales).
+enum Epi { kEpiI32 = 0, kEpiBf16 = 1, kEpiBf16Row = 2, kEpiF16 = 3, kEpiF16Row = 4,
+           kEpiDefBf16 = 5, kEpiDefF16 = 6 };
 
 __device__ inline uint32_t pack_f16x2(float a, float b) {
   const _Float16 ha = static_cast<_Float16>(a);   // v_cvt_f16_f32: round to nearest even
@@ -229,7 +259,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
   __shared__ __attribute__((aligned(16))) char lds[T::kLdsBytes];
   constexpr bool DEQUANT = EPI != kEpiI32;
   constexpr bool kRowScale = EPI == kEpiBf16Row || EPI == kEpiF16Row;
-  constexpr bool kF16 = EPI == kEpiF16 || EPI == kEpiF16Row;
+  constexpr bool kDefault = EPI == kEpiDefBf16 || EPI == kEpiDefF16;
+  constexpr bool kF16 = EPI == kEpiF16 || EPI == kEpiF16Row || EPI == kEpiDefF16;
+  constexpr int OP = EPI == kEpiDefBf16 ? kOpBf16 : EPI == kEpiDefF16 ? kOpF16 : kOpI8;
 
   int tn, tm;
   tile_coords<T>(tiles_n, tiles_m, tn, tm);
@@ -287,7 +319,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
   const int a_base = wn * T::kWaveN * T::BK;
   const int b_base = T::BN * T::BK + wm * T::kWaveM * T::BK;
 
-  using acc_t = typename Acc<T::MF>::type;
+  using acc_t = typename Acc<T::MF, OP>::type;
   acc_t acc[T::TN][T::TM];
 #pragma unroll
   for (int i = 0; i < T::TN; ++i)
@@ -300,7 +332,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
   const int m_lane0 = wm * T::kWaveM + (lane & (T::MF - 1));
 #pragma unroll
   for (int j = 0; j < T::TM; ++j)
-    alpha[j] = DEQUANT ? x_scale[min(m0 + m_lane0 + j * T::MF, M - 1)] : 0.0f;
+    alpha[j] = DEQUANT && !kDefault ? x_scale[min(m0 + m_lane0 + j * T::MF, M - 1)] : 0.0f;
   (void)w_scale;
 
   // Fragments are double-buffered per MFMA k step (a "unit": 32 bytes of K
@@ -323,7 +355,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
 #pragma unroll
     for (int i = 0; i < T::TN; ++i)
 #pragma unroll
-      for (int j = 0; j < T::TM; ++j) acc[i][j] = mfma<T::MF>(f.a[i], f.b[j], acc[i][j]);
+      for (int j = 0; j < T::TM; ++j) acc[i][j] = mfma<T::MF, OP>(f.a[i], f.b[j], acc[i][j]);
   };
   // Issue order inside a unit: each MFMA is followed by one of the unit's
   // loads (direct-to-LDS loads first, then LDS fragment reads), so the loads
@@ -457,7 +489,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
     uint16_t* y = static_cast<uint16_t*>(out);
     // Scales and bias for this lane's outputs: every load is issued before
     // the first one is used, so their latency is paid once per tile.
-    const float sw = kRowScale ? 1.0f : *w_scale;
+    const float sw = kRowScale || kDefault ? 1.0f : *w_scale;
     // bias of n = n0 + n_loc + i*MF + 8*g + e, e = 0..3: 8-byte loads when the
     // four values are in range and aligned, else element by element
     uint2 bias4[T::TN][kGroups];
@@ -515,7 +547,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
 #pragma unroll
         for (int j = 0; j < T::TM; ++j) {
           float v[4];
-          if constexpr (kRowScale) {
+          if constexpr (kDefault) {
+            // default path: fp32 product sum plus the bias, one rounding below
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] + b[e];
+          } else if constexpr (kRowScale) {
             // alpha = s_x[m] * s_w[n], one fp32 product per output
             const float sc[4] = {ws4[g].x, ws4[g].y, ws4[g].z, ws4[g].w};
 #pragma unroll
@@ -528,8 +564,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
           }
           if constexpr (kF16) {
             // the output is fp16_rne of the fp32 result: keep v in fp32 here,
-            // or the compiler fuses fma and conversion into v_fma_mixlo_f16,
-            // which rounds the exact value to fp16 once
+            // or the compiler fuses the fma (or add) and the conversion into
+            // v_fma_mixlo_f16, which rounds the exact value to fp16 once
 #pragma unroll
             for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(v[e]));
           }
@@ -676,6 +712,16 @@ hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc, int
                            int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   return launch_gemm<kEpiI32>(xq, nullptr, wq, nullptr, nullptr, acc, M, N, K, stream);
+}
+
+hipError_t launch_gemm_default(const uint16_t* x, const uint16_t* wu, const uint16_t* bias, uint16_t* y,
+                               bool f16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  // operands travel as bytes: a row of K 16-bit values is 2K bytes
+  const auto* a = reinterpret_cast<const int8_t*>(x);
+  const auto* b = reinterpret_cast<const int8_t*>(wu);
+  return f16 ? launch_gemm<kEpiDefF16>(a, nullptr, b, nullptr, bias, y, M, N, 2 * K, stream)
+             : launch_gemm<kEpiDefBf16>(a, nullptr, b, nullptr, bias, y, M, N, 2 * K, stream);
 }
 
 }  // namespace convrot

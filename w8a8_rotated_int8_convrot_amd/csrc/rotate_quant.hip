@@ -380,6 +380,85 @@ int num_cus() {
   return n;
 }
 
+// ---------------------------------------------------------------- default path
+// Unpacking of a rotated int8 weight for the default (dequantizing) path
+// (page "int8 Compute", "What stays on the default path": such layers keep
+// unpacking their weights): every row is dequantized (s * q in fp32) and
+// rotated back by R, which is its own inverse (symmetric and orthogonal), so
+// the same butterfly in the same order applies; the result is rounded to
+// bf16 or fp16.  One workgroup per row, the row streamed in segments of
+// 256 * 8 * CPT values (no pass over the whole row is needed).
+template <int G, int CPT, bool OutF16>
+__global__ __launch_bounds__(kThreads) void unpack_rows_kernel(
+    const int8_t* __restrict__ wq, int64_t K, const float* __restrict__ w_scale, int row_scale,
+    uint16_t* __restrict__ out) {
+  constexpr int kSegment = kThreads * 8 * CPT;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane_in_group = tid % (G / 8);
+  const float s = w_scale[row_scale ? row : 0];
+  const int8_t* qr = wq + row * K;
+  uint16_t* orow = out + row * K;
+  float v[CPT][8];
+  for (int64_t base = 0; base < K; base += kSegment) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int64_t e = base + (static_cast<int64_t>(j) * kThreads + tid) * 8;
+      if (e < K) {
+        const uint2 w = *reinterpret_cast<const uint2*>(qr + e);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[j][i] = s * static_cast<float>(static_cast<int8_t>(w.x >> (8 * i)));
+          v[j][4 + i] = s * static_cast<float>(static_cast<int8_t>(w.y >> (8 * i)));
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int64_t e = base + (static_cast<int64_t>(j) * kThreads + tid) * 8;
+      if (e < K) {
+        rotate_chunk<G>(v[j], lane_in_group);
+        if constexpr (OutF16) {
+          // round the fp32 value to fp16: keep it in fp32 here, or the
+          // compiler fuses the last multiply and the conversion into one
+          // mixed-precision instruction that rounds the exact product once
+#pragma unroll
+          for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(v[j][i]));
+        }
+        uint32_t p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint16_t lo, hi;
+          if constexpr (OutF16) {
+            lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[j][2 * i]));
+            hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[j][2 * i + 1]));
+          } else {
+            lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[j][2 * i]));
+            hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[j][2 * i + 1]));
+          }
+          p[i] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+        }
+        *reinterpret_cast<uint4*>(orow + e) = make_uint4(p[0], p[1], p[2], p[3]);
+      }
+    }
+  }
+}
+
+template <int G, bool OutF16>
+hipError_t launch_unpack_g(const int8_t* wq, const float* w_scale, bool row_scale, int64_t N, int64_t K,
+                           uint16_t* out, hipStream_t stream) {
+  const int64_t slots = (K + kThreads * 8 - 1) / (kThreads * 8);
+  const dim3 grid(static_cast<uint32_t>(N)), block(kThreads);
+  const int rs = row_scale ? 1 : 0;
+  if (slots <= 1)
+    hipLaunchKernelGGL((unpack_rows_kernel<G, 1, OutF16>), grid, block, 0, stream, wq, K, w_scale, rs, out);
+  else if (slots <= 2)
+    hipLaunchKernelGGL((unpack_rows_kernel<G, 2, OutF16>), grid, block, 0, stream, wq, K, w_scale, rs, out);
+  else
+    hipLaunchKernelGGL((unpack_rows_kernel<G, 4, OutF16>), grid, block, 0, stream, wq, K, w_scale, rs, out);
+  return hipGetLastError();
+}
+
 template <int G, int CPT, typename In, int MODE>
 hipError_t launch_rows(const In* x, int64_t rows, int64_t K, int8_t* q, float* scale,
                        uint32_t* cell, hipStream_t stream) {
@@ -440,6 +519,15 @@ hipError_t rotate_quant_16(const In16* x, int64_t M, int64_t K, int group, int8_
 }
 
 }  // namespace
+
+hipError_t launch_unpack_weight(const int8_t* wq, const float* w_scale, bool row_scale, int64_t N,
+                                int64_t K, int group, bool out_f16, uint16_t* out, hipStream_t stream) {
+  if (group == 128)
+    return out_f16 ? launch_unpack_g<128, true>(wq, w_scale, row_scale, N, K, out, stream)
+                   : launch_unpack_g<128, false>(wq, w_scale, row_scale, N, K, out, stream);
+  return out_f16 ? launch_unpack_g<256, true>(wq, w_scale, row_scale, N, K, out, stream)
+                 : launch_unpack_g<256, false>(wq, w_scale, row_scale, N, K, out, stream);
+}
 
 hipError_t launch_rotate_quant(const uint16_t* x, int64_t M, int64_t K, int group, int8_t* q,
                                float* scale, hipStream_t stream) {
