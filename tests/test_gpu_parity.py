@@ -247,7 +247,7 @@ def test_empty_batch_is_a_no_op(B):
     assert y.shape == (0, 8)
 
 
-@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16"])
+@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "half"])
 @pytest.mark.parametrize("M,N,K", [(300, 1001, 384), (513, 1000, 1024), (1111, 777, 640)])
 def test_every_gemm_tile_is_bit_exact(B, tile, M, N, K, monkeypatch):
     # the tile shape is a performance choice: every one must give the same bytes
@@ -265,6 +265,31 @@ def test_every_gemm_tile_is_bit_exact(B, tile, M, N, K, monkeypatch):
     acc_ref = oracle.gemm_i32(a, b)
     assert np.array_equal(acc, acc_ref)
     assert np.all(same_bf16(bits_of(y), oracle.epilogue(acc_ref, s_x, s_w, bias)))
+
+
+@pytest.mark.parametrize("M", [2000, 2112])
+def test_half_height_tail_split(B, M):
+    # M = 2000 or 2112, N = 12288: 352 tiles of 384 x 192 would leave the second
+    # round 96 of 256 full, so token rows [0, 1536) run as 384 x 192 tiles and
+    # the rest as 384 x 96 tiles (ragged for M = 2000) in a second launch;
+    # rows on both sides of the split and at the end are compared
+    N, K = 12288, 384
+    a = rand_i8((M, K), M)
+    b = rand_i8((N, K), 3)
+    r = np.random.default_rng(M)
+    s_x = (r.random(M) * 0.2 + 1e-3).astype(np.float32)
+    s_w = np.float32(1.3e-4)
+    bias = synth.to_bf16_bits(r.standard_normal(N) * 0.01)
+    ad, bd = torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)
+    acc = B.convrot_gemm_i32(ad, bd)
+    y = B.convrot_gemm_dequant(ad, torch.from_numpy(s_x).to(DEV), bd, torch.tensor([s_w], device=DEV),
+                               to_dev_bf16(bias, DEV))
+    rows = np.unique(np.concatenate([[0, 191, 192, 1535, 1536, 1537, 1631, 1632, M - 2, M - 1],
+                                     r.choice(M, 24, replace=False)]))
+    ridx = torch.from_numpy(rows).to(DEV)
+    acc_ref = oracle.gemm_i32(a[rows], b)
+    assert np.array_equal(acc[ridx].cpu().numpy(), acc_ref)
+    assert np.all(same_bf16(bits_of(y[ridx]), oracle.epilogue(acc_ref, s_x[rows], s_w, bias)))
 
 
 @pytest.mark.parametrize("reps", [1, 700])       # row kernel; block kernel (M*K > 2^21)

@@ -129,6 +129,11 @@ using TileSkinny16 = Tile<16, 16, 1, 1, 16, 1, 24>;
 // 128 bytes of K, and the direct-to-LDS loads fetch 128 contiguous bytes of
 // a row (eight lanes) per request instead of 64.
 using TileWide128 = Tile<384, 192, 4, 3, 32, 4, 2, 128>;
+// 384 x 96 (each wave 96 x 32): the last, at most half-full round of 384 x 192
+// tiles runs as these half-height tiles instead, so it takes about half a
+// round (M = 4608, N = 9216: 504 tiles in two rounds, then 144 half tiles;
+// 163 us instead of 171 with 256 x 256 tiles over three rounds).
+using TileWideHalf = Tile<384, 96, 4, 3, 32, 4, 2, 128>;
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 
@@ -639,12 +644,12 @@ hipError_t launch_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
   return hipGetLastError();
 }
 
-// Tile choice: CONVROT_GEMM_TILE=big|big8|wide|mid|skinny forces one (the
-// result does not depend on it).  Otherwise: M <= 32 streams the weight with
-// the skinny tile; layers with fewer than 64 large tiles use 128x128; else
-// the cost of a large tile is the number of rounds its tiles take over the
-// 256 CUs times the work of one tile, and the cheaper of 256x256 and 384x192
-// wins.
+// Tile choice: CONVROT_GEMM_TILE=big|big8|wide|wide128|mid|skinny|skinny16|half
+// forces one (the result does not depend on it).  Otherwise: M <= 32 streams
+// the weight with a skinny tile; layers with fewer than 64 large tiles use
+// 128x128; else the cost of a large tile is the number of rounds its tiles
+// take over the 256 CUs times the work of one tile, and the cheaper of
+// 256x256 and 384x192 (with its half-height tail, below) wins.
 int forced_tile() {
   const char* e = getenv("CONVROT_GEMM_TILE");
   if (e == nullptr) return 0;
@@ -655,6 +660,7 @@ int forced_tile() {
   if (strcmp(e, "skinny") == 0) return 5;
   if (strcmp(e, "wide128") == 0) return 6;
   if (strcmp(e, "skinny16") == 0) return 7;
+  if (strcmp(e, "half") == 0) return 8;
   return 0;
 }
 
@@ -665,12 +671,33 @@ int64_t tile_cost(int64_t M, int64_t N, int64_t bn, int64_t bm) {
   return (tiles + kCUs - 1) / kCUs * bn * bm;
 }
 
+// Token tiles of 384 x 192 that run in whole rounds.  When their last round
+// would be at most half full and the remaining token rows fit one round of
+// 384 x 96 tiles, only the whole rounds use 384 x 192 and the rest of M runs
+// as half-height tiles; otherwise every token tile is 384 x 192.
+int64_t wide_main_m(int64_t M, int64_t N) {
+  const int64_t tn = (N + 383) / 384, tm = (M + 191) / 192;
+  const int64_t tiles = tn * tm, rounds = (tiles + kCUs - 1) / kCUs;
+  const int64_t last = tiles - (rounds - 1) * kCUs;
+  if (rounds < 2 || 2 * last > kCUs) return tm;
+  const int64_t main_m = (rounds - 1) * kCUs / tn;
+  const int64_t tail = (M - main_m * 192 + 95) / 96 * tn;
+  return main_m > 0 && tail <= kCUs ? main_m : tm;
+}
+
+// Cost of 384 x 192 tiles, counting the half-height tail as half a round.
+int64_t wide_cost(int64_t M, int64_t N) {
+  const int64_t tn = (N + 383) / 384, tm = (M + 191) / 192, main_m = wide_main_m(M, N);
+  if (main_m == tm) return tile_cost(M, N, 384, 192);
+  return ((main_m * tn + kCUs - 1) / kCUs * 2 + 1) * 384 * 96;
+}
+
 int pick_tile(int64_t M, int64_t N) {
   if (M <= 16) return 7;
   if (M <= 32) return 5;
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles < 64) return 3;   // tiny layers: more, smaller tiles
-  return tile_cost(M, N, 384, 192) < tile_cost(M, N, 256, 256) ? 6 : 1;
+  return wide_cost(M, N) < tile_cost(M, N, 256, 256) ? 6 : 1;
 }
 
 template <int EPI>
@@ -683,7 +710,19 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
   if (t == 2) return launch_tile<TileBig8, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 4) return launch_tile<TileWide, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 5) return launch_tile<TileSkinny, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
-  if (t == 6) return launch_tile<TileWide128, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 6) {
+    // whole rounds of 384 x 192, then (if any) the rest of M as 384 x 96;
+    // K counts bytes, and the output rows are 2 (dequant) or 4 (int32) bytes
+    const int64_t split = wide_main_m(M, N) * 192;
+    if (split >= M) return launch_tile<TileWide128, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+    hipError_t e = launch_tile<TileWide128, EPI>(xq, x_scale, wq, w_scale, bias, out, split, N, K, stream);
+    if (e != hipSuccess) return e;
+    const int64_t out_elem = EPI == kEpiI32 ? 4 : 2;
+    return launch_tile<TileWideHalf, EPI>(xq + split * K, x_scale ? x_scale + split : nullptr, wq, w_scale,
+                                          bias, static_cast<char*>(out) + split * N * out_elem, M - split, N,
+                                          K, stream);
+  }
+  if (t == 8) return launch_tile<TileWideHalf, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 7) return launch_tile<TileSkinny16, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   return launch_tile<TileMid, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
 }
