@@ -27,7 +27,9 @@ CPU oracle timed on a bounded sample of token rows.  Beside them:
                 row-wise-scale variant of the whole layer at this shape;
                 the default (dequantizing) path at this shape -- unpack the
                 int8 weight to bf16, then the bf16 product -- beside the
-                int8 layer; and the guarded layer once its check has run.
+                int8 layer; the guarded layer once its check has run; and
+                one synthetic DiT denoising step's 240-layer linear stack on
+                both paths (the analogue of the pages' per-step timings).
 """
 import argparse
 import hashlib
@@ -205,6 +207,77 @@ def streamed_path(binding, torch, dev, stream, x, wq, s_w, g, bias, n_layers=8, 
             "copy_only_GBps": round(wbytes / (t_copy * 1e-3) / 1e9, 1)}
 
 
+def stack_path(binding, synth, torch, dev, stream, g, reps=2):
+    """One synthetic DiT denoising step's linear stack at 1024^2: 60 blocks of
+    QKV (3072 -> 9216), out-projection (3072 -> 3072), MLP up (3072 -> 12288)
+    and down (12288 -> 3072) at M = 4608 tokens, 240 independent int8 weights
+    (6.79 GB) resident in HBM.  Weights are N(0, 0.02^2) drawn on the device
+    from a seeded generator per layer and prepared once; the block input and
+    the attention-output stand-in are N(0, 1) rows rescaled to a per-token
+    absmax drawn from U[5, 30]; the down projection reads the up projection's
+    output.  The same stack runs on the int8 layer and on the default path
+    (weight unpacked on every call, bf16 product), each timed with HIP events
+    over whole passes."""
+    M = synth.STACK_M
+    gen = torch.Generator(device=dev)
+    layers = []
+    for b in range(synth.STACK_BLOCKS):
+        for li, (kind, K, N) in enumerate(synth.STACK_LAYERS):
+            gen.manual_seed(0xC0517 + 5000 + 10 * (4 * b + li))
+            w = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
+            wq, s_w = binding.convrot_prepare_weight(w, g)
+            bias = (torch.randn(N, generator=gen, device=dev) * 0.01).to(torch.bfloat16)
+            layers.append((kind, wq, s_w, bias))
+            del w
+
+    def tokens(seed):
+        gen.manual_seed(seed)
+        x = torch.randn((M, 3072), generator=gen, device=dev)
+        a = 5.0 + 25.0 * torch.rand((M, 1), generator=gen, device=dev)
+        return (x * (a / x.abs().amax(dim=1, keepdim=True))).to(torch.bfloat16)
+
+    x_in, x_attn = tokens(0xC0517 + 5001), tokens(0xC0517 + 5002)
+    outs = {n: torch.empty((M, n), dtype=torch.bfloat16, device=dev) for n in (9216, 3072, 12288)}
+    ws = torch.empty(max(binding.convrot_linear_workspace(M, K, N) for _, K, N in synth.STACK_LAYERS),
+                     dtype=torch.uint8, device=dev)
+    ws_def = torch.empty(max(binding.convrot_default_workspace(K, N) for _, K, N in synth.STACK_LAYERS),
+                         dtype=torch.uint8, device=dev)
+
+    def run(fn, wsp):
+        y_down = torch.empty((M, 3072), dtype=torch.bfloat16, device=dev)
+        for kind, wq, s_w, bias in layers:
+            if kind == "qkv":
+                fn(x_in, wq, s_w, g, bias, out=outs[9216], workspace=wsp)
+            elif kind == "out":
+                fn(x_attn, wq, s_w, g, bias, out=outs[3072], workspace=wsp)
+            elif kind == "up":
+                fn(x_in, wq, s_w, g, bias, out=outs[12288], workspace=wsp)
+            else:
+                fn(outs[12288], wq, s_w, g, bias, out=y_down, workspace=wsp)
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, wsp):
+        run(fn, wsp)
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(reps):
+            run(fn, wsp)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    t_int8 = timed(binding.convrot_linear, ws)
+    t_def = timed(binding.convrot_default_linear, ws_def)
+    ops = 2.0 * M * sum(K * N for _, K, N in synth.STACK_LAYERS) * synth.STACK_BLOCKS
+    wbytes = sum(wq.numel() for _, wq, _, _ in layers)
+    del layers
+    return {"workload": f"{synth.STACK_BLOCKS} DiT blocks x (QKV 3072->9216, out 3072->3072, up 3072->12288, "
+                        f"down 12288->3072) at M={M}, {wbytes / 1e9:.2f} GB of int8 weights resident",
+            "ms": round(t_int8, 3), "value": round(ops / (t_int8 * 1e-3) / 1e12, 1), "unit": "TOPS",
+            "default_path_ms": round(t_def, 3), "int8_speedup": round(t_def / t_int8, 3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -291,6 +364,7 @@ def main():
 
     small = small_m_paths(binding, synth, np, torch, dev, stream, g, args.steps)
     streamed = streamed_path(binding, torch, dev, stream, x, wq, s_w, g, bias)
+    stack = stack_path(binding, synth, torch, dev, stream, g)
 
     # the same layer in fp16 with one weight scale per output channel
     # (convrot_linear_ex), timed the same way as the step
@@ -391,6 +465,7 @@ def main():
                          "product_tflops": round(ops / ((def_ms - unpack_ms) * 1e-3) / 1e12, 1),
                          "bf16_peak_tflops": 2500.0,
                          "int8_layer_speedup": round(def_ms / step_ms_events, 3)},
+        "dit_step_stack": stack,
         "guarded": {"entry": "convrot_linear_guarded", "ms": round(guarded_ms, 5),
                     "check_rel_error": round(guard_state["last_error"], 5),
                     "fallback": guard_state["fallback"]},
