@@ -212,8 +212,10 @@ __global__ __launch_bounds__(kThreads) void rotate_rows_kernel(
 // workgroup's rows are staged through LDS so that a lane can hold a whole
 // block in registers and run all seven butterfly stages in place (no lane
 // exchanges); for g = 256 the eighth stage pairs neighbouring lanes.  Both
-// HBM streams stay coalesced: 16-byte loads of consecutive input chunks into
-// LDS, and 16-byte stores of consecutive code chunks out of it.
+// HBM streams stay coalesced: each wave moves its own 64 blocks, 1 KB of
+// consecutive input per direct-to-LDS instruction and 16-byte stores of
+// consecutive code chunks, so the only workgroup barrier is the one that
+// completes the per-row maxima (rows cross wave boundaries).
 //
 // Codes: rne(v / s) with the quotient correctly rounded, computed with a
 // reciprocal and two fused multiply-adds instead of a full division per
@@ -240,19 +242,24 @@ __global__ __launch_bounds__(256) void rotq_block_kernel(
   const int nchunk = nblk * 16;
 
   if (tid < rows_per_wg) row_amax[tid] = 0u;
+  __syncthreads();   // the row maxima start at zero before any wave adds to them
+  // Each wave loads exactly its own 64 blocks (lane b of the workgroup owns
+  // block b), so no wave waits for another before it computes: waves whose
+  // data arrives first start their arithmetic while the rest still load.
+  // Direct-to-LDS: instruction u of wave w fills the 64 LDS slots
+  // p = 1024 w + 64 u + lane; slot p holds chunk (p & 15) ^ (b & 15) of block
+  // b = p >> 4 (the XOR layout the reads below expect).
   const uint4* src = reinterpret_cast<const uint4*>(x + row0 * K);
-  constexpr int kInFlight = 8;
-  for (int base = 0; base < nchunk; base += 256 * kInFlight) {
-    uint4 r[kInFlight];
-#pragma unroll
-    for (int u = 0; u < kInFlight; ++u) r[u] = src[min(base + u * 256 + tid, nchunk - 1)];
-#pragma unroll
-    for (int u = 0; u < kInFlight; ++u) {
-      const int c = base + u * 256 + tid;
-      if (c < nchunk) tile[(c >> 4) * 16 + ((c & 15) ^ ((c >> 4) & 15))] = r[u];
-    }
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wchunks = max(0, min(64, nblk - 64 * wave)) * 16;
+  for (int u = 0; u * 64 < wchunks; ++u) {
+    const int p = 1024 * wave + 64 * u + lane;
+    const int b = p >> 4;
+    if (64 * u + lane < wchunks)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + b * 16 + ((p & 15) ^ (b & 15))),
+                                       (__attribute__((address_space(3))) void*)(tile + 1024 * wave + 64 * u), 16, 0, 0);
   }
-  __syncthreads();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const int b = tid;
   const bool active = b < nblk;
@@ -356,10 +363,12 @@ __global__ __launch_bounds__(256) void rotq_block_kernel(
       }
     }
   }
-  __syncthreads();
+  // this wave stores its own blocks' codes (LDS operations of one wave
+  // complete in order, so its code writes above are visible to its reads)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   uint4* dstq = reinterpret_cast<uint4*>(q + row0 * K);
-  const int ncode = nblk * 8;
-  for (int c = tid; c < ncode; c += 256) {
+  const int wcodes = wchunks / 2;
+  for (int c = 512 * wave + lane; c < 512 * wave + wcodes; c += 64) {
     const int bb = c >> 3, j = c & 7;
     dstq[c] = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(codes) + bb * 128)[j ^ ((bb >> 1) & 7)];
   }
