@@ -29,7 +29,10 @@ CPU oracle timed on a bounded sample of token rows.  Beside them:
                 int8 weight to bf16, then the bf16 product -- beside the
                 int8 layer; the guarded layer once its check has run; and
                 one synthetic DiT denoising step's 240-layer linear stack on
-                both paths (the analogue of the pages' per-step timings).
+                both paths (the analogue of the pages' per-step timings); the
+                whole layer on the other workload shapes (tiny, QKV, MLP down,
+                2048^2 MLP up); and single steps, each timed alone, with and
+                without a 512 MB write before it (median and minimum).
 """
 import argparse
 import hashlib
@@ -278,6 +281,52 @@ def stack_path(binding, synth, torch, dev, stream, g, reps=2):
             "default_path_ms": round(t_def, 3), "int8_speedup": round(t_def / t_int8, 3)}
 
 
+def configs_path(binding, synth, np, torch, dev, stream, g, reps=20):
+    """The whole layer (convrot_linear) on the other workload shapes of the
+    pages' configurations, with the same seeded inputs as the parity tests:
+    each timed with HIP events over `reps` back-to-back calls."""
+    out = {}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for name in ("tiny", "qkv", "mlp_down", "hires_up"):
+        L = synth.make_layer(name, g=g)
+        x = torch.from_numpy(L.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        bias = torch.from_numpy(L.bias_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        w = torch.from_numpy(L.w).to(dev)
+        wq, s_w = binding.convrot_prepare_weight(w, g)
+        del w
+        y = torch.empty((L.M, L.N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(binding.convrot_linear_workspace(L.M, L.K, L.N), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            binding.convrot_linear(x, wq, s_w, g, bias, out=y, workspace=ws)
+        ev[0].record(stream)
+        for _ in range(reps):
+            binding.convrot_linear(x, wq, s_w, g, bias, out=y, workspace=ws)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        tops = 2.0 * L.M * L.N * L.K / (ms * 1e-3) / 1e12
+        out[name] = {"M": L.M, "K": L.K, "N": L.N, "ms": round(ms, 5), "value": round(tops, 1), "unit": "TOPS",
+                     "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2)}
+        del x, bias, wq, s_w, y, ws
+    return out
+
+
+def per_step_times(torch, stream, step, n, flush=None):
+    """Median and minimum of n single steps, each between its own pair of HIP
+    events; with `flush`, a 512 MB buffer is written before each step (outside
+    the events) so that no operand is left in the L2s or the MALL."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        if flush is not None:
+            flush.fill_(1)
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"median_ms": round(t[len(t) // 2], 5), "min_ms": round(t[0], 5), "steps": n}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -365,6 +414,11 @@ def main():
     small = small_m_paths(binding, synth, np, torch, dev, stream, g, args.steps)
     streamed = streamed_path(binding, torch, dev, stream, x, wq, s_w, g, bias)
     stack = stack_path(binding, synth, torch, dev, stream, g)
+    configs = configs_path(binding, synth, np, torch, dev, stream, g)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    single = {"unflushed": per_step_times(torch, stream, step, 20),
+              "flushed": per_step_times(torch, stream, step, 20, flush=flush_buf)}
+    del flush_buf
 
     # the same layer in fp16 with one weight scale per output channel
     # (convrot_linear_ex), timed the same way as the step
@@ -466,6 +520,8 @@ def main():
                          "bf16_peak_tflops": 2500.0,
                          "int8_layer_speedup": round(def_ms / step_ms_events, 3)},
         "dit_step_stack": stack,
+        "configs": configs,
+        "single_step": single,
         "guarded": {"entry": "convrot_linear_guarded", "ms": round(guarded_ms, 5),
                     "check_rel_error": round(guard_state["last_error"], 5),
                     "fallback": guard_state["fallback"]},
