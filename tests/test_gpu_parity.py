@@ -170,7 +170,9 @@ def test_linear_end_to_end(B, name, g):
     assert np.array_equal(wq.cpu().numpy(), wq_ref), "weight codes"
     assert s_w.item() == float(s_w_ref), "weight scale"
 
-    rows = np.arange(L.M) if L.M <= 256 else synth.sample_rows(L.M, 64, L.M + L.N)
+    # 256 seeded rows for the 2048^2 layer and the stack, 64 for the others
+    count = 256 if name.startswith(("hires", "stack")) else 64
+    rows = np.arange(L.M) if L.M <= 256 else synth.sample_rows(L.M, count, L.M + L.N)
     y_ref, q_ref, s_ref = oracle.linear_rows(L.x_bits, rows, wq_ref, s_w_ref, L.g, L.bias_bits)
     ridx = torch.from_numpy(rows).to(DEV)
     q_gpu = q[ridx].cpu().numpy()
