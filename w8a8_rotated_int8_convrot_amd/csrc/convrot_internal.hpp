@@ -1,7 +1,10 @@
 // convrot_internal.hpp -- shared declarations of the HIP library (not part of
-// the C ABI).  Kernels live in rotate_quant.hip and gemm_i8.hip (and a
-// measurement loop in mfma_probe.hip); argument
-// checking and dispatch live in convrot_api.hip.
+// the C ABI).  Kernels live in rotate_quant.hip (rotation + quantization, and
+// the default path's weight unpacking), gemm_i8.hip (the int8 GEMM with its
+// epilogues, and the default path's bf16/fp16 product on the same tiles),
+// default_path.hip (the guarded layer's check) and mfma_probe.hip (a
+// measurement loop); argument checking, dispatch and the guard state live in
+// convrot_api.hip.
 #pragma once
 
 #include <hip/hip_runtime.h>

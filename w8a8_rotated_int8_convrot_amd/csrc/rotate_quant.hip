@@ -286,20 +286,28 @@ __global__ __launch_bounds__(256) void rotq_block_kernel(
         }
       }
     }
+    // the normalisation constant, negated where a lane holds a negated sum
+    float c = RotScale<G>::value;
     if constexpr (G == 256) {
       // stage h = 128: element i of the even block (a) pairs with element i
       // of the odd block of the same group, held by the neighbouring lane
-      // (blocks per row are even for g = 256, so both lanes are active)
+      // (blocks per row are even for g = 256, so both lanes are active).
+      // The even lane needs RN(a + b), the odd lane RN(a - b); one fma
+      // RN(v + sgn * p) gives RN(a + b) on the even lane and RN(b - a) =
+      // -RN(a - b) on the odd lane (rounding to nearest is symmetric), and
+      // the odd lane's multiply by -c undoes the sign: RN(RN(a - b) * c).
       const bool upper = (b & 1) != 0;
+      const float sgn = upper ? -1.0f : 1.0f;
+      c = upper ? -c : c;
 #pragma unroll
       for (int i = 0; i < kBlockElems; ++i) {
         const float p = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[i]), 0xB1, 0xF, 0xF, false));
-        v[i] = upper ? (p - v[i]) : (v[i] + p);
+        v[i] = __builtin_fmaf(p, sgn, v[i]);
       }
     }
 #pragma unroll
     for (int i = 0; i < kBlockElems; ++i) {
-      v[i] = v[i] * RotScale<G>::value;
+      v[i] = v[i] * c;
       amax = fmaxf(amax, fabsf(v[i]));
     }
     atomicMax(&row_amax[lrow], __float_as_uint(amax));   // amax >= 0: bit order = value order
