@@ -239,7 +239,6 @@ __global__ __launch_bounds__(256) void rotq_block_kernel(
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
   const int rows = static_cast<int>(min(static_cast<int64_t>(rows_per_wg), M - row0));
   const int nblk = rows * bpr;
-  const int nchunk = nblk * 16;
 
   if (tid < rows_per_wg) row_amax[tid] = 0u;
   __syncthreads();   // the row maxima start at zero before any wave adds to them
