@@ -433,8 +433,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
     }
   };
 
+  if constexpr (T::kStages > 2) {
 #pragma unroll
-  for (int s = 0; s < T::kStages - 1; ++s) issue_slab(min(s, KT - 1), s);
+    for (int s = 0; s < T::kStages - 1; ++s) issue_slab(min(s, KT - 1), s);
+  }
   KFrag f0, f1;
   if constexpr (T::kStages == 2) {
     // Two stages: slab kt+2 is issued at the boundary between slabs kt and
