@@ -18,6 +18,10 @@ namespace convrot {
 // an int32 accumulator cannot overflow.
 constexpr int64_t kMaxK = 131072;
 
+// Compute units of the current device (read once; 256 on MI355X), which the
+// launch shapes are balanced over.
+int num_cus();
+
 // ---------------------------------------------------------------- rotate + quant
 
 // Per-token rotate + quantize of a bf16 [M, K] activation into int8 codes and

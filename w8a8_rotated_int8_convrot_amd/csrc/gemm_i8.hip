@@ -670,9 +670,8 @@ int forced_tile() {
   return 0;
 }
 
-constexpr int64_t kCUs = 256;
-
 int64_t tile_cost(int64_t M, int64_t N, int64_t bn, int64_t bm) {
+  const int64_t kCUs = num_cus();
   const int64_t tiles = ((N + bn - 1) / bn) * ((M + bm - 1) / bm);
   return (tiles + kCUs - 1) / kCUs * bn * bm;
 }
@@ -682,6 +681,7 @@ int64_t tile_cost(int64_t M, int64_t N, int64_t bn, int64_t bm) {
 // 384 x 96 tiles, only the whole rounds use 384 x 192 and the rest of M runs
 // as half-height tiles; otherwise every token tile is 384 x 192.
 int64_t wide_main_m(int64_t M, int64_t N) {
+  const int64_t kCUs = num_cus();
   const int64_t tn = (N + 383) / 384, tm = (M + 191) / 192;
   const int64_t tiles = tn * tm, rounds = (tiles + kCUs - 1) / kCUs;
   const int64_t last = tiles - (rounds - 1) * kCUs;
@@ -693,6 +693,7 @@ int64_t wide_main_m(int64_t M, int64_t N) {
 
 // Cost of 384 x 192 tiles, counting the half-height tail as half a round.
 int64_t wide_cost(int64_t M, int64_t N) {
+  const int64_t kCUs = num_cus();
   const int64_t tn = (N + 383) / 384, tm = (M + 191) / 192, main_m = wide_main_m(M, N);
   if (main_m == tm) return tile_cost(M, N, 384, 192);
   return ((main_m * tn + kCUs - 1) / kCUs * 2 + 1) * 384 * 96;

@@ -383,19 +383,6 @@ __global__ __launch_bounds__(256) void rotq_block_kernel(
 
 __global__ void zero_word_kernel(uint32_t* p) { *p = 0u; }
 
-int num_cus() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
-  }
-  return n;
-}
-
 // ---------------------------------------------------------------- default path
 // Unpacking of a rotated int8 weight for the default (dequantizing) path
 // (page "int8 Compute", "What stays on the default path": such layers keep
@@ -535,6 +522,19 @@ hipError_t rotate_quant_16(const In16* x, int64_t M, int64_t K, int group, int8_
 }
 
 }  // namespace
+
+int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
 
 hipError_t launch_unpack_weight(const int8_t* wq, const float* w_scale, bool row_scale, int64_t N,
                                 int64_t K, int group, bool out_f16, uint16_t* out, hipStream_t stream) {
