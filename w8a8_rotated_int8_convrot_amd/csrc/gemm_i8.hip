@@ -27,6 +27,12 @@
 //    - BK = 64, three or more stages, prefetched kStages-1 slabs ahead.
 //    Fragments are double-buffered per MFMA k step: while one k step's MFMAs
 //    run from one register set, the LDS reads of the next fill the other.
+//    A load's address is a scalar base (the tile's first operand row plus the
+//    slab's K offset) and a fixed 32-bit per-lane offset, and its LDS
+//    destination (M0) is computed by the scalar unit: nothing on the vector
+//    side sits between a slab's loads, so issuing them does not hold up the
+//    MFMAs that follow (2-3.5 % faster than 64-bit per-lane addresses
+//    rebuilt in one register pair before every load).
 //    Stage reuse is guarded by `s_waitcnt vmcnt` (this wave's loads of the
 //    needed slab have landed) and one `s_barrier` (so have everyone else's,
 //    and everyone is done with the stage about to be refilled).
@@ -278,14 +284,23 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // the wave index is uniform across the wave: keep it in a scalar register,
+  // so that LDS destinations (M0) are computed by the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave / T::WM, wm = wave % T::WM;
 
   // ---- direct-to-LDS sources: instruction j of this wave fills LDS rows
   // [16*i, 16*i + 16) of its operand (i = wave * loads + j); lane L lands in
   // row 16*i + L/4, stored chunk L%4, and so fetches global chunk
   // (L%4) ^ ((row >> 1) & 3) of that row.
-  const int8_t* src[T::kLoads];
+  // Each load's global address is a per-tile scalar base (the tile's first
+  // row of the operand, plus the slab's K offset) and a per-lane 32-bit
+  // offset that stays fixed for the whole K loop (at most BN rows of K bytes,
+  // far below 2^31), so no vector instruction recomputes an address between
+  // the loads of a slab.
+  const int8_t* a_tile = wq + static_cast<int64_t>(n0) * K;
+  const int8_t* b_tile = xq + static_cast<int64_t>(m0) * K;
+  uint32_t off[T::kLoads];
   int dst[T::kLoads];
 #pragma unroll
   for (int j = 0; j < T::kLoads; ++j) {
@@ -294,10 +309,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
     const int row = T::kRowsPerLoad * i + lane / T::kRowChunks;
     const int chunk = (lane % T::kRowChunks) ^ swz<T::MF, T::BK>(row);
     if (is_a) {
-      src[j] = wq + static_cast<int64_t>(min(n0 + row, N - 1)) * K + chunk * 16;
+      off[j] = static_cast<uint32_t>((min(n0 + row, N - 1) - n0) * K + chunk * 16);
       dst[j] = i * T::kRowsPerLoad * T::BK;
     } else {
-      src[j] = xq + static_cast<int64_t>(min(m0 + row, M - 1)) * K + chunk * 16;
+      off[j] = static_cast<uint32_t>((min(m0 + row, M - 1) - m0) * K + chunk * 16);
       dst[j] = T::BN * T::BK + i * T::kRowsPerLoad * T::BK;
     }
   }
@@ -307,7 +322,12 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
     const int64_t k0 = static_cast<int64_t>(slab) * T::BK;
 #pragma unroll
     for (int j = 0; j < T::kLoads; ++j) {
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(src[j] + k0),
+      const int8_t* base = (j < T::kALoads ? a_tile : b_tile) + k0;
+      // keep the offset a 32-bit register at the load (the empty asm makes it
+      // opaque, so the compiler cannot widen it ahead of the loop and the load
+      // takes the scalar base + 32-bit vector offset form)
+      asm volatile("" : "+v"(off[j]));
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off[j]),
                                        (lds_void_t*)(lds + stage * T::kStageBytes + dst[j]),
                                        16, 0, 0);
     }
