@@ -724,7 +724,12 @@ int pick_tile(int64_t M, int64_t N) {
   if (M <= 32) return 5;
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles < 64) return 3;   // tiny layers: more, smaller tiles
-  return wide_cost(M, N) < tile_cost(M, N, 256, 256) ? 6 : 1;
+  // the 256 x 256 tile (one wave per SIMD) wins only by a clear margin: it
+  // was as fast or slower on every shape measured, also where its cost is
+  // lower (M = 4608, N = 3072: 184 us for 216 tiles against 180 us for 192 at
+  // K = 12288, 57-59 against 52-53 us at K = 3072; 3072 x 9216 x 4096: 142.5
+  // against 138.5 us; 1536 x 3072 x 3072: 42.8 against 38.5 us)
+  return wide_cost(M, N) * 100 < tile_cost(M, N, 256, 256) * 115 ? 6 : 1;
 }
 
 template <int EPI>
