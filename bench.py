@@ -411,6 +411,30 @@ def main():
     probe_ms = ev[0].elapsed_time(ev[1]) / 5
     probe_tops = probe_blocks * 4 * probe_iters * 16 * 65536 / (probe_ms * 1e-3) / 1e12
 
+    # the same GEMM and the same register-only MFMA loop on constant codes
+    # (every activation and weight byte 1): the board is power-limited, and
+    # the clock falls with operand bit activity, so this is the rate the
+    # kernel reaches when its operands toggle least
+    q1 = torch.ones_like(q)
+    wq1 = torch.ones_like(wq)
+    for _ in range(3):
+        binding.convrot_gemm_dequant(q1, s, wq1, s_w, bias, out=y)
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        binding.convrot_gemm_dequant(q1, s, wq1, s_w, bias, out=y)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    const_gemm_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    for _ in range(2):
+        binding.convrot_probe_mfma_i8(q1, wq1, probe_blocks, probe_iters, out=probe_out)
+    ev[0].record(stream)
+    for _ in range(5):
+        binding.convrot_probe_mfma_i8(q1, wq1, probe_blocks, probe_iters, out=probe_out)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    const_probe_tops = probe_blocks * 4 * probe_iters * 16 * 65536 / (ev[0].elapsed_time(ev[1]) / 5 * 1e-3) / 1e12
+    del q1, wq1
+
     small = small_m_paths(binding, synth, np, torch, dev, stream, g, args.steps)
     streamed = streamed_path(binding, torch, dev, stream, x, wq, s_w, g, bias)
     stack = stack_path(binding, synth, torch, dev, stream, g)
@@ -466,6 +490,7 @@ def main():
     del ws_def, wu, ws_g
 
     ops = 2.0 * M * N * K
+    ops_total = ops
     value = ops / step_s / 1e12
     achieved = ops / (gemm_ms * 1e-3) / 1e12
     traffic = measured_traffic()
@@ -520,6 +545,12 @@ def main():
                          "bf16_peak_tflops": 2500.0,
                          "int8_layer_speedup": round(def_ms / step_ms_events, 3)},
         "dit_step_stack": stack,
+        "power_check": {"note": "same kernels on constant codes (every byte 1): the clock falls with operand "
+                                "bit activity under the board's power limit",
+                        "gemm_ms_workload_codes": round(gemm_ms, 5), "gemm_ms_constant_codes": round(const_gemm_ms, 5),
+                        "gemm_tops_constant_codes": round(ops_total / (const_gemm_ms * 1e-3) / 1e12, 1),
+                        "mfma_loop_tops_workload_codes": round(probe_tops, 1),
+                        "mfma_loop_tops_constant_codes": round(const_probe_tops, 1)},
         "configs": configs,
         "single_step": single,
         "guarded": {"entry": "convrot_linear_guarded", "ms": round(guarded_ms, 5),
