@@ -248,15 +248,25 @@ __global__ __launch_bounds__(256) void rotq_block_kernel(
   // Direct-to-LDS: instruction u of wave w fills the 64 LDS slots
   // p = 1024 w + 64 u + lane; slot p holds chunk (p & 15) ^ (b & 15) of block
   // b = p >> 4 (the XOR layout the reads below expect).
-  const uint4* src = reinterpret_cast<const uint4*>(x + row0 * K);
-  const int wave = tid >> 6, lane = tid & 63;
+  // Addresses: the wave's first chunk is a scalar base (the wave index is
+  // uniform), and the lane's chunk within instruction u depends on u only
+  // through (4 u) & 15, so four fixed 32-bit lane offsets cover every u; the
+  // LDS destination (M0) is computed by the scalar unit.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wchunks = max(0, min(64, nblk - 64 * wave)) * 16;
-  for (int u = 0; u * 64 < wchunks; ++u) {
-    const int p = 1024 * wave + 64 * u + lane;
-    const int b = p >> 4;
-    if (64 * u + lane < wchunks)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + b * 16 + ((p & 15) ^ (b & 15))),
+  const char* wbase = reinterpret_cast<const char*>(x + row0 * K) + static_cast<int64_t>(wave) * 64 * 256;
+  uint32_t loff[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    loff[r] = static_cast<uint32_t>(((lane >> 4) * 16 + ((lane & 15) ^ ((4 * r + (lane >> 4)) & 15))) * 16);
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    if (u * 64 >= wchunks) break;
+    if (64 * u + lane < wchunks) {
+      asm volatile("" : "+v"(loff[u & 3]));
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(wbase + u * 1024 + loff[u & 3]),
                                        (__attribute__((address_space(3))) void*)(tile + 1024 * wave + 64 * u), 16, 0, 0);
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
