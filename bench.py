@@ -20,7 +20,10 @@ CPU oracle timed on a bounded sample of token rows.  Beside them:
   mfma_ceiling  the rate a register-only MFMA loop sustains on this machine
                 with this workload's own int8 codes (the board's power limit
                 lowers the clock with operand toggling), and the GEMM's
-                fraction of it;
+                fraction of it; power_check adds the board power and GFX
+                clock read with amd-smi while the GEMM runs back to back on
+                the workload's codes and on constant codes, and the int8 peak
+                scaled to the clock the workload's codes sustain;
   paths         the HBM-bound steps against 8 TB/s: rotate+quant of this
                 workload, and the few-token layer (M=16, K=4096, N=12288)
                 with its weight read from HBM on every call; the fp16 /
@@ -46,6 +49,7 @@ sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA: 5.0 POP/s
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E: 8 TB/s
+MAX_GFX_MHZ = 2400.0           # MI355X peak engine clock, at which the 5.0 POP/s holds
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_mlp_up.json")
 GEMM_SOURCES = [os.path.join(ROOT, "w8a8_rotated_int8_convrot_amd", "csrc", "gemm_i8.hip")]
 
@@ -117,6 +121,51 @@ def cpu_baseline(L, budget_s):
             "sample": f"{done} seeded token rows of the M={L.M} batch (whole layer per row: "
                       f"rotate+quantize, int8 GEMM against all N={L.N} channels, epilogue), "
                       f"{t_used:.1f} s, single-threaded C oracle"}
+
+
+def smi_sample():
+    """One reading of the board's socket power (W) and the mean GFX clock over
+    the XCDs (MHz) from `amd-smi metric`, or None where the tool gives none."""
+    import re
+    import shutil
+    import subprocess
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    try:
+        r = subprocess.run([exe, "metric", "-p", "-c"], capture_output=True, text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    p = re.search(r"SOCKET_POWER:\s*(\d+(?:\.\d+)?)\s*W", r.stdout)
+    clks = [float(v) for v in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+(?:\.\d+)?)\s*MHz", r.stdout)]
+    if p is None or not clks:
+        return None
+    return float(p.group(1)), sum(clks) / len(clks)
+
+
+def clocks_under_load(torch, fn, call_ms, seconds=3.0):
+    """Launch fn back to back for about `seconds` of GPU time and read power
+    and clock three times from a second thread once the board has settled."""
+    import threading
+    samples = []
+
+    def sampler():
+        time.sleep(1.0)
+        for _ in range(3):
+            r = smi_sample()
+            if r is not None:
+                samples.append(r)
+            time.sleep(0.2)
+
+    t = threading.Thread(target=sampler)
+    t.start()
+    for _ in range(max(int(seconds * 1e3 / call_ms), 1)):
+        fn()
+    torch.cuda.synchronize()
+    t.join()
+    if not samples:
+        return None
+    return {"socket_power_w": round(sum(p for p, _ in samples) / len(samples), 1),
+            "gfx_clock_mhz": round(sum(c for _, c in samples) / len(samples), 1),
+            "samples": len(samples)}
 
 
 def small_m_paths(binding, synth, np, torch, dev, stream, g, steps):
@@ -433,6 +482,11 @@ def main():
     ev[1].record(stream)
     torch.cuda.synchronize()
     const_probe_tops = probe_blocks * 4 * probe_iters * 16 * 65536 / (ev[0].elapsed_time(ev[1]) / 5 * 1e-3) / 1e12
+    # board power and GFX clock while the GEMM runs back to back, on the
+    # workload's codes and on constant codes
+    clk_work = clocks_under_load(torch, lambda: binding.convrot_gemm_dequant(q, s, wq, s_w, bias, out=y), gemm_ms)
+    clk_const = clocks_under_load(torch, lambda: binding.convrot_gemm_dequant(q1, s, wq1, s_w, bias, out=y),
+                                  const_gemm_ms)
     del q1, wq1
 
     small = small_m_paths(binding, synth, np, torch, dev, stream, g, args.steps)
@@ -550,7 +604,13 @@ def main():
                         "gemm_ms_workload_codes": round(gemm_ms, 5), "gemm_ms_constant_codes": round(const_gemm_ms, 5),
                         "gemm_tops_constant_codes": round(ops_total / (const_gemm_ms * 1e-3) / 1e12, 1),
                         "mfma_loop_tops_workload_codes": round(probe_tops, 1),
-                        "mfma_loop_tops_constant_codes": round(const_probe_tops, 1)},
+                        "mfma_loop_tops_constant_codes": round(const_probe_tops, 1),
+                        "gemm_clocks_workload_codes": clk_work, "gemm_clocks_constant_codes": clk_const,
+                        "max_gfx_clock_mhz": MAX_GFX_MHZ,
+                        "int8_peak_at_gemm_clock_tops": (round(INT8_PEAK_TOPS * clk_work["gfx_clock_mhz"] / MAX_GFX_MHZ, 1)
+                                                         if clk_work else None),
+                        "gemm_frac_at_gemm_clock": (round(achieved / (INT8_PEAK_TOPS * clk_work["gfx_clock_mhz"]
+                                                                      / MAX_GFX_MHZ), 4) if clk_work else None)},
         "configs": configs,
         "single_step": single,
         "guarded": {"entry": "convrot_linear_guarded", "ms": round(guarded_ms, 5),
