@@ -26,7 +26,8 @@ CPU oracle timed on a bounded sample of token rows.  Beside them:
                 scaled to the clock the workload's codes sustain;
   paths         the HBM-bound steps against 8 TB/s: rotate+quant of this
                 workload, and the few-token layer (M=16, K=4096, N=12288)
-                with its weight read from HBM on every call; the fp16 /
+                with its weight read from HBM on every call (and its GEMM at
+                M = 32, 64, 128); the fp16 /
                 row-wise-scale variant of the whole layer at this shape;
                 the default (dequantizing) path at this shape -- unpack the
                 int8 weight to bf16, then the bf16 product -- beside the
@@ -60,6 +61,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--group", type=int, default=128, choices=(128, 256))
+    p.add_argument("--clock-seconds", type=float, default=3.0,
+                   help="seconds of back-to-back GEMMs per operand set while amd-smi reads power and "
+                        "clock (0 skips the reading)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample (0 disables the cpu_baseline leg)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -130,8 +134,11 @@ def smi_sample():
     import shutil
     import subprocess
     exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    # amd-smi is a Python script: run it with this interpreter rather than
+    # through its `env` shebang, so the child starts as python directly
     try:
-        r = subprocess.run([exe, "metric", "-p", "-c"], capture_output=True, text=True, timeout=30)
+        r = subprocess.run([sys.executable, os.path.realpath(exe), "metric", "-p", "-c"],
+                           capture_output=True, text=True, timeout=30)
     except (OSError, subprocess.SubprocessError):
         return None
     p = re.search(r"SOCKET_POWER:\s*(\d+(?:\.\d+)?)\s*W", r.stdout)
@@ -172,7 +179,7 @@ def small_m_paths(binding, synth, np, torch, dev, stream, g, steps):
     """The few-token case (M=16, K=4096, N=12288), which streams the weight:
     GEMM+epilogue and the whole layer timed over 8 copies of the prepared
     weight in turn (403 MB, more than the 256 MB last-level cache), so every
-    call reads its weight from HBM."""
+    call reads its weight from HBM; and the GEMM alone at M = 32, 64, 128."""
     L = synth.make_layer("small_m", g=g)
     M, K, N = L.M, L.K, L.N
     x = torch.from_numpy(L.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -198,6 +205,15 @@ def small_m_paths(binding, synth, np, torch, dev, stream, g, steps):
     gemm_ms = timed(lambda w: binding.convrot_gemm_dequant(q, s, w, s_w, bias, out=y))
     lin_ms = timed(lambda w: binding.convrot_linear(x, w, s_w, g, bias, out=y, workspace=ws))
     gemm_bytes = N * K + M * K + 2 * M * N + 2 * N + 4 * M
+    # the same weight stream with a few dozen tokens (the 16 rows repeated)
+    q8, s8 = binding.convrot_rotate_quant(x.repeat(8, 1), g)
+    more = {}
+    for m in (32, 64, 128):
+        ym = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+        ms = timed(lambda w: binding.convrot_gemm_dequant(q8[:m], s8[:m], w, s_w, bias, out=ym))
+        nb = N * K + m * K + 2 * m * N + 2 * N + 4 * m
+        more[f"M={m}"] = {"ms": round(ms, 5), "bytes": nb, "achieved": round(nb / (ms * 1e-3) / 1e9, 1),
+                          "frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     lin_bytes = gemm_bytes + 3 * M * K + 4 * M
     wl = f"M={M} tokens, K={K}, N={N}, group {g}, weight read from HBM (8 rotating copies)"
     return {
@@ -209,6 +225,10 @@ def small_m_paths(binding, synth, np, torch, dev, stream, g, steps):
         "small_m_linear": {"workload": wl, "ms": round(lin_ms, 5), "bytes": lin_bytes,
                            "achieved": round(lin_bytes / (lin_ms * 1e-3) / 1e9, 1),
                            "unit": "GB/s"},
+        "few_token_gemm": {"kernel": "gemm_i8_kernel (64-channel tiles, the batch in one token tile)",
+                           "workload": f"M = 32, 64, 128 tokens, K={K}, N={N}, weight read from HBM "
+                                       "(8 rotating copies)", "bound": "hbm", "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", **more},
     }
 
 
@@ -484,9 +504,12 @@ def main():
     const_probe_tops = probe_blocks * 4 * probe_iters * 16 * 65536 / (ev[0].elapsed_time(ev[1]) / 5 * 1e-3) / 1e12
     # board power and GFX clock while the GEMM runs back to back, on the
     # workload's codes and on constant codes
-    clk_work = clocks_under_load(torch, lambda: binding.convrot_gemm_dequant(q, s, wq, s_w, bias, out=y), gemm_ms)
-    clk_const = clocks_under_load(torch, lambda: binding.convrot_gemm_dequant(q1, s, wq1, s_w, bias, out=y),
-                                  const_gemm_ms)
+    clk_work = clk_const = None
+    if args.clock_seconds > 0:
+        clk_work = clocks_under_load(torch, lambda: binding.convrot_gemm_dequant(q, s, wq, s_w, bias, out=y),
+                                     gemm_ms, args.clock_seconds)
+        clk_const = clocks_under_load(torch, lambda: binding.convrot_gemm_dequant(q1, s, wq1, s_w, bias, out=y),
+                                      const_gemm_ms, args.clock_seconds)
     del q1, wq1
 
     small = small_m_paths(binding, synth, np, torch, dev, stream, g, args.steps)

@@ -106,7 +106,8 @@ def test_default_linear_within_bound(io, mode, M, N, K):
     assert_default_close(host_bits(y), x, np.arange(M), wu, bias, io, K)
 
 
-@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "half"])
+@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "half",
+                                  "m32", "m64", "m128"])
 def test_default_product_on_every_tile(tile, monkeypatch):
     monkeypatch.setenv("CONVROT_GEMM_TILE", tile)
     M, N, K, g = 300, 1001, 640, 128

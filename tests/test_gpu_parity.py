@@ -228,7 +228,10 @@ def test_bit_identical_run_to_run(B):
     assert torch.equal(q, q2) and torch.equal(s, s2)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (1, 3, 256), (2, 5, 128), (16, 12288, 4096), (63, 130, 512)])
+# few-token shapes on each automatic choice: 16 x 16 (M <= 16), 64 x 64 and
+# 64 x 128 (many channels), 32 x 32 and 64 x 32 (few channels, ragged N)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (1, 3, 256), (2, 5, 128), (16, 12288, 4096), (63, 130, 512),
+                                   (40, 12288, 1024), (100, 9216, 512), (64, 3072, 1536), (128, 3000, 384)])
 def test_small_and_ragged_shapes(B, M, N, K):
     r = np.random.default_rng(M + N + K)
     xb = rand_bf16(M, K, M + K, outliers=0)
@@ -249,7 +252,8 @@ def test_empty_batch_is_a_no_op(B):
     assert y.shape == (0, 8)
 
 
-@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "half"])
+@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "half",
+                                  "m32", "m64", "m128"])
 @pytest.mark.parametrize("M,N,K", [(300, 1001, 384), (513, 1000, 1024), (1111, 777, 640)])
 def test_every_gemm_tile_is_bit_exact(B, tile, M, N, K, monkeypatch):
     # the tile shape is a performance choice: every one must give the same bytes

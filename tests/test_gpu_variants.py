@@ -116,7 +116,7 @@ def test_linear_variants_end_to_end(io, mode, M, K, N, g):
     assert oracle.nrmse(widen(y_ref), ref) < 0.05
 
 
-@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16"])
+@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "m32", "m64", "m128"])
 def test_every_tile_runs_the_variant_epilogues(tile, monkeypatch):
     monkeypatch.setenv("CONVROT_GEMM_TILE", tile)
     r = np.random.default_rng(5)

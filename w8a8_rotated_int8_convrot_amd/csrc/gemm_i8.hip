@@ -144,6 +144,20 @@ using TileWide128 = Tile<384, 192, 4, 3, 32, 8, 2, 128>;
 // round (M = 4608, N = 9216: 504 tiles in two rounds, then 144 half tiles;
 // 163 us instead of 171 with 256 x 256 tiles over three rounds).
 using TileWideHalf = Tile<384, 96, 4, 3, 32, 4, 2, 128>;
+// A few dozen tokens (16 < M <= 128), where streaming the weight is still most
+// of the cost.  With many output channels (N/64 >= 96), 64 channels per
+// workgroup and the whole batch in one token tile, so each weight row leaves
+// HBM once: 64 x 64 (four waves of 32 x 32) for M <= 64 and 64 x 128 (four
+// waves of 32 x 64) for M <= 128, eight 64-byte stages, two workgroups per CU
+// (weight from HBM, K = 4096, N = 12288: M = 64 in 16.4 us instead of 28.2
+// with 128 x 128 tiles, M = 128 in 20.9 instead of 29.0).  With fewer
+// channels, narrower tiles give more workgroups: 32 x 32 (TileSkinny) up to
+// M = 64 and 64 x 32 (two waves of 32 x 32, twelve stages) up to M = 128
+// (K = 12288, N = 3072: M = 64 in 24.3 us instead of 72.5, M = 128 in 30.6
+// instead of 74.7).
+using TileM64 = Tile<64, 64, 2, 2, 32, 1, 8>;
+using TileM128 = Tile<64, 128, 2, 2, 32, 1, 8>;
+using TileM32 = Tile<64, 32, 2, 1, 32, 1, 12>;
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 
@@ -670,12 +684,14 @@ hipError_t launch_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
   return hipGetLastError();
 }
 
-// Tile choice: CONVROT_GEMM_TILE=big|big8|wide|wide128|mid|skinny|skinny16|half
-// forces one (the result does not depend on it).  Otherwise: M <= 32 streams
-// the weight with a skinny tile; layers with fewer than 64 large tiles use
-// 128x128; else the cost of a large tile is the number of rounds its tiles
-// take over the 256 CUs times the work of one tile, and the cheaper of
-// 256x256 and 384x192 (with its half-height tail, below) wins.
+// Tile choice: CONVROT_GEMM_TILE=big|big8|wide|wide128|mid|skinny|skinny16|half|m32|m64|m128
+// forces one (the result does not depend on it).  Otherwise: M <= 16 streams
+// the weight with the 16 x 16 tile and M <= 128 with the tiles above that
+// keep the batch in one token tile (or, with few channels, in tiles of 32
+// tokens); larger layers with fewer than 64 large tiles use 128x128; else the
+// cost of a large tile is the number of rounds its tiles take over the 256
+// CUs times the work of one tile, and the cheaper of 256x256 and 384x192
+// (with its half-height tail, below) wins.
 int forced_tile() {
   const char* e = getenv("CONVROT_GEMM_TILE");
   if (e == nullptr) return 0;
@@ -687,6 +703,9 @@ int forced_tile() {
   if (strcmp(e, "wide128") == 0) return 6;
   if (strcmp(e, "skinny16") == 0) return 7;
   if (strcmp(e, "half") == 0) return 8;
+  if (strcmp(e, "m32") == 0) return 10;
+  if (strcmp(e, "m64") == 0) return 11;
+  if (strcmp(e, "m128") == 0) return 12;
   return 0;
 }
 
@@ -721,7 +740,10 @@ int64_t wide_cost(int64_t M, int64_t N) {
 
 int pick_tile(int64_t M, int64_t N) {
   if (M <= 16) return 7;
-  if (M <= 32) return 5;
+  if (M <= 128) {
+    if ((N + 63) / 64 >= 96) return M <= 64 ? 11 : 12;
+    return M <= 64 ? 5 : 10;
+  }
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles < 64) return 3;   // tiny layers: more, smaller tiles
   // the 256 x 256 tile (one wave per SIMD) wins only by a clear margin: it
@@ -756,6 +778,9 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
   }
   if (t == 8) return launch_tile<TileWideHalf, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 7) return launch_tile<TileSkinny16, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 10) return launch_tile<TileM32, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 11) return launch_tile<TileM64, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 12) return launch_tile<TileM128, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   return launch_tile<TileMid, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
 }
 
