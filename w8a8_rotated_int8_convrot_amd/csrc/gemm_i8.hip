@@ -688,10 +688,10 @@ hipError_t launch_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
 // forces one (the result does not depend on it).  Otherwise: M <= 16 streams
 // the weight with the 16 x 16 tile and M <= 128 with the tiles above that
 // keep the batch in one token tile (or, with few channels, in tiles of 32
-// tokens); larger layers with fewer than 64 large tiles use 128x128; else the
-// cost of a large tile is the number of rounds its tiles take over the 256
-// CUs times the work of one tile, and the cheaper of 256x256 and 384x192
-// (with its half-height tail, below) wins.
+// tokens); larger layers with fewer 384 x 192 tiles than half the CUs use
+// 128 x 128 or 64 x 128 tiles; else the cost of a large tile is the number of
+// rounds its tiles take over the 256 CUs times the work of one tile, and the
+// cheaper of 256x256 and 384x192 (with its half-height tail, below) wins.
 int forced_tile() {
   const char* e = getenv("CONVROT_GEMM_TILE");
   if (e == nullptr) return 0;
@@ -744,13 +744,20 @@ int pick_tile(int64_t M, int64_t N) {
     if ((N + 63) / 64 >= 96) return M <= 64 ? 11 : 12;
     return M <= 64 ? 5 : 10;
   }
-  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles < 64) return 3;   // tiny layers: more, smaller tiles
+  // Fewer 384 x 192 tiles than half the CUs: smaller tiles give more
+  // workgroups, 128 x 128 (two per CU), or 64 x 128 where even those would
+  // fill less than half the CUs (weight from HBM: 512 x 12288 x 4096 in 51 us
+  // instead of 59, 1536 x 3072 x 3072 in 31 instead of 38, 512 x 3072 x 12288
+  // in 52 instead of 73; from 128 large tiles on, 384 x 192 is faster again:
+  // 768 x 12288 x 4096 in 64 us against 76 with 128 x 128)
+  const int64_t kCUs = num_cus();
+  if (2 * ((M + 191) / 192) * ((N + 383) / 384) < kCUs)
+    return 2 * ((M + 127) / 128) * ((N + 127) / 128) < kCUs ? 12 : 3;
   // the 256 x 256 tile (one wave per SIMD) wins only by a clear margin: it
   // was as fast or slower on every shape measured, also where its cost is
   // lower (M = 4608, N = 3072: 184 us for 216 tiles against 180 us for 192 at
   // K = 12288, 57-59 against 52-53 us at K = 3072; 3072 x 9216 x 4096: 142.5
-  // against 138.5 us; 1536 x 3072 x 3072: 42.8 against 38.5 us)
+  // against 138.5 us)
   return wide_cost(M, N) * 100 < tile_cost(M, N, 256, 256) * 115 ? 6 : 1;
 }
 
