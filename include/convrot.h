@@ -120,7 +120,7 @@ size_t convrot_linear_workspace(int64_t M, int64_t K, int64_t N);
  *   workspace ws_bytes of device scratch.  Tokens are processed in slices of
  *             S = min(M, 2N, ws_bytes / (K + 4) rounded down to a multiple
  *             of 16 (or M if smaller)) rows; a workspace too small for one
- *             16-row slice (or for M rows if M < 16) is CONVROT_EWORKSPACE.
+ *             slice of min(M, 2N, 16) rows is CONVROT_EWORKSPACE.
  *             The result does not depend on S.
  * Per slice: one rotate+quant launch, then one GEMM+epilogue launch. */
 int convrot_linear(const void *x_bf16, int64_t M, int64_t K,

@@ -5,6 +5,7 @@
 // only its checking calls synchronise (with their stream).
 #include "../../include/convrot.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -183,7 +184,8 @@ int linear_impl(const char* who, const void* x_in, int io_dtype, int64_t M, int6
   if (!aligned16(x_in) || !aligned16(wq) || !aligned16(y_out) || (workspace && !aligned16(workspace)))
     return fail(CONVROT_EALIGN, "%s: x, wq, y and workspace must be 16-byte aligned", who);
   const int64_t S = workspace ? slice_rows(M, K, N, ws_bytes) : 0;
-  const int64_t need = M < 16 ? M : 16;
+  // one slice of 16 rows, or of the whole slice height min(M, 2N) if that is less
+  const int64_t need = std::min<int64_t>(std::min<int64_t>(M, 2 * N), 16);
   if (S < need)
     return fail(CONVROT_EWORKSPACE, "%s: workspace of %zu bytes holds %lld rows; at least %lld needed "
                 "(convrot_linear_workspace gives %zu)", who, ws_bytes, static_cast<long long>(S),
@@ -320,7 +322,7 @@ int convrot_linear_streamed(const convrot_stream_layer* layers, int n_layers, vo
       return fail(CONVROT_EWORKSPACE, "%s: layer %d: N*K=%lld bytes exceed slot_bytes=%zu", who, i,
                   static_cast<long long>(L.N * L.K), slot_bytes);
     const int64_t S = workspace ? slice_rows(L.M, L.K, L.N, ws_bytes) : 0;
-    const int64_t need = L.M < 16 ? L.M : 16;
+    const int64_t need = std::min<int64_t>(std::min<int64_t>(L.M, 2 * L.N), 16);
     if (S < need)
       return fail(CONVROT_EWORKSPACE, "%s: layer %d: workspace of %zu bytes holds %lld rows; at least %lld "
                   "needed", who, i, ws_bytes, static_cast<long long>(S), static_cast<long long>(need));

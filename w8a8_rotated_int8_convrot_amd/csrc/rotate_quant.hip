@@ -13,7 +13,9 @@
 // to 1/sqrt(g).  Every add happens in that order on the GPU too, so the codes
 // are bit-identical to a sequential evaluation of the same butterfly.
 //
-// Layout on the device: one workgroup of 256 threads per row.  A thread owns
+// Row kernel (small batches, weights, rows past 32768 elements; the
+// token-block kernel below has its own layout): one workgroup of 256 threads
+// per row.  A thread owns
 // up to CPT chunks of 8 consecutive elements (16-byte bf16 loads, 8-byte code
 // stores, both coalesced across the wave); chunk c of a segment of
 // 256 * 8 * CPT elements sits in thread c % 256.  Stages h = 1, 2, 4 stay inside a thread; stage h = 8 * 2^t pairs
@@ -208,186 +210,177 @@ __global__ __launch_bounds__(kThreads) void rotate_rows_kernel(
 }
 
 // ---------------------------------------------------------------- token blocks
-// Activation path for K <= 32768: one lane per 128-element block.  The
-// workgroup's rows are staged through LDS so that a lane can hold a whole
-// block in registers and run all seven butterfly stages in place (no lane
-// exchanges); for g = 256 the eighth stage pairs neighbouring lanes.  Both
-// HBM streams stay coalesced: each wave moves its own 64 blocks, 1 KB of
-// consecutive input per direct-to-LDS instruction and 16-byte stores of
-// consecutive code chunks, so the only workgroup barrier is the one that
-// completes the per-row maxima (rows cross wave boundaries).
+// Activation path for K <= 32768.  The workgroup's rows are staged through
+// LDS by direct-to-LDS loads (each wave moves its own 32 blocks, 1 KB of
+// consecutive input per instruction), and two lanes hold one 128-element
+// block in registers: lane 2b + h takes elements [64h, 64h + 64) of block b.
+// Stages h' = 1..32 stay in the lane; stage 64 pairs the two lanes (one DPP
+// exchange); for g = 256 stage 128 pairs the same half of blocks b and b ^ 1
+// (lanes two apart).  A lane that must keep a - b while it holds b computes
+// RN(b - a) = -RN(a - b) with the same fma its partner uses for RN(a + b) and
+// carries the sign into the final multiply (rounding to nearest is
+// symmetric), so every add is the one the sequential butterfly does.  With
+// 64 values per lane a wave needs about 94 registers, so twice as many waves
+// share a SIMD as with a whole block per lane (4608 x 3072: 13.2 -> 11.7 us;
+// 4608 x 12288: 43.5 -> 36.8 us; identical codes and scales).  The codes go
+// back through LDS so that every wave stores its own blocks as 16-byte
+// chunks of consecutive codes; the only workgroup barrier completes the
+// per-row maxima (rows cross wave boundaries).
 //
 // Codes: rne(v / s) with the quotient correctly rounded, computed with a
 // reciprocal and two fused multiply-adds instead of a full division per
 // element (rows whose scale is too small for a normal reciprocal divide).
 constexpr int kBlockElems = 128;
-constexpr int kMaxBlocksPerWg = 256;                 // one block per thread
+constexpr int kMaxBlocksPerWg = 256;                 // two lanes per block: 512 lanes
 constexpr int kMaxBlockK = kMaxBlocksPerWg * kBlockElems;
 constexpr int64_t kSmallBatchElems = int64_t{1} << 21;
 
 template <int G, typename In16>
-__global__ __launch_bounds__(256) void rotq_block_kernel(
+__global__ __launch_bounds__(512) void rotq_block_kernel(
     const In16* __restrict__ x, int64_t M, int K, int rows_per_wg,
     int8_t* __restrict__ q, float* __restrict__ scale) {
-  // bf16 input tile: block b occupies 16 chunks of 16 bytes; chunk j is stored
-  // at j ^ (b & 15) so that 32 lanes reading chunk j of 32 consecutive blocks
-  // hit each 16-byte bank slot exactly twice (conflict-free on gfx950).
-  __shared__ __attribute__((aligned(16))) uint4 tile[kMaxBlocksPerWg * 16];
+  // the input tile, 256 bytes per block of the workgroup (sized at launch)
+  extern __shared__ __attribute__((aligned(16))) uint4 tile[];
   __shared__ uint32_t row_amax[kMaxBlocksPerWg];
   const int tid = threadIdx.x;
-  const int bpr = K / kBlockElems;                    // blocks per row
+  const int bpr = K / kBlockElems;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
   const int rows = static_cast<int>(min(static_cast<int64_t>(rows_per_wg), M - row0));
   const int nblk = rows * bpr;
 
   if (tid < rows_per_wg) row_amax[tid] = 0u;
-  __syncthreads();   // the row maxima start at zero before any wave adds to them
-  // Each wave loads exactly its own 64 blocks (lane b of the workgroup owns
-  // block b), so no wave waits for another before it computes: waves whose
-  // data arrives first start their arithmetic while the rest still load.
-  // Direct-to-LDS: instruction u of wave w fills the 64 LDS slots
-  // p = 1024 w + 64 u + lane; slot p holds chunk (p & 15) ^ (b & 15) of block
-  // b = p >> 4 (the XOR layout the reads below expect).
-  // Addresses: the wave's first chunk is a scalar base (the wave index is
-  // uniform), and the lane's chunk within instruction u depends on u only
-  // through (4 u) & 15, so four fixed 32-bit lane offsets cover every u; the
-  // LDS destination (M0) is computed by the scalar unit.
+  __syncthreads();
+  // wave w loads its own 32 blocks: instruction u fills LDS slots
+  // p = 512 w + 64 u + lane, slot p holding chunk (p & 15) ^ (b & 15) of
+  // block b = p >> 4
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int wchunks = max(0, min(64, nblk - 64 * wave)) * 16;
-  const char* wbase = reinterpret_cast<const char*>(x + row0 * K) + static_cast<int64_t>(wave) * 64 * 256;
+  const int wchunks = max(0, min(32, nblk - 32 * wave)) * 16;
+  const char* wbase = reinterpret_cast<const char*>(x + row0 * K) + static_cast<int64_t>(wave) * 32 * 256;
   uint32_t loff[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     loff[r] = static_cast<uint32_t>(((lane >> 4) * 16 + ((lane & 15) ^ ((4 * r + (lane >> 4)) & 15))) * 16);
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
+  for (int u = 0; u < 8; ++u) {
     if (u * 64 >= wchunks) break;
     if (64 * u + lane < wchunks) {
       asm volatile("" : "+v"(loff[u & 3]));
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(wbase + u * 1024 + loff[u & 3]),
-                                       (__attribute__((address_space(3))) void*)(tile + 1024 * wave + 64 * u), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(tile + 512 * wave + 64 * u), 16, 0, 0);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  const int b = tid;
+  const int b = tid >> 1, half = tid & 1;
   const bool active = b < nblk;
   const int lrow = active ? b / bpr : 0;
-  float v[kBlockElems];
+  float v[64];
   float amax = 0.0f;
+  // the normalisation constant times the sign this lane's values carry
+  float c = RotScale<G>::value;
   if (active) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint4 w = tile[b * 16 + (j ^ (b & 15))];
-      v[8 * j + 0] = in_lo<In16>(w.x); v[8 * j + 1] = in_hi<In16>(w.x);
-      v[8 * j + 2] = in_lo<In16>(w.y); v[8 * j + 3] = in_hi<In16>(w.y);
-      v[8 * j + 4] = in_lo<In16>(w.z); v[8 * j + 5] = in_hi<In16>(w.z);
-      v[8 * j + 6] = in_lo<In16>(w.w); v[8 * j + 7] = in_hi<In16>(w.w);
+    for (int jj = 0; jj < 8; ++jj) {
+      const uint4 w = tile[b * 16 + ((8 * half + jj) ^ (b & 15))];
+      v[8 * jj + 0] = in_lo<In16>(w.x); v[8 * jj + 1] = in_hi<In16>(w.x);
+      v[8 * jj + 2] = in_lo<In16>(w.y); v[8 * jj + 3] = in_hi<In16>(w.y);
+      v[8 * jj + 4] = in_lo<In16>(w.z); v[8 * jj + 5] = in_hi<In16>(w.z);
+      v[8 * jj + 6] = in_lo<In16>(w.w); v[8 * jj + 7] = in_hi<In16>(w.w);
     }
 #pragma unroll
-    for (int h = 1; h < kBlockElems; h <<= 1) {
+    for (int h = 1; h < 64; h <<= 1) {
 #pragma unroll
-      for (int i = 0; i < kBlockElems; ++i) {
+      for (int i = 0; i < 64; ++i) {
         if ((i & h) == 0) {
-          const float a = v[i], c = v[i + h];
-          v[i] = a + c;
-          v[i + h] = a - c;
+          const float a = v[i], d = v[i + h];
+          v[i] = a + d;
+          v[i + h] = a - d;
         }
       }
     }
-    // the normalisation constant, negated where a lane holds a negated sum
-    float c = RotScale<G>::value;
-    if constexpr (G == 256) {
-      // stage h = 128: element i of the even block (a) pairs with element i
-      // of the odd block of the same group, held by the neighbouring lane
-      // (blocks per row are even for g = 256, so both lanes are active).
-      // The even lane needs RN(a + b), the odd lane RN(a - b); one fma
-      // RN(v + sgn * p) gives RN(a + b) on the even lane and RN(b - a) =
-      // -RN(a - b) on the odd lane (rounding to nearest is symmetric), and
-      // the odd lane's multiply by -c undoes the sign: RN(RN(a - b) * c).
-      const bool upper = (b & 1) != 0;
-      const float sgn = upper ? -1.0f : 1.0f;
-      c = upper ? -c : c;
+    {  // stage 64: the lower half keeps RN(a + b), the upper RN(b - a)
+      const float sgn = half ? -1.0f : 1.0f;
+      c = half ? -c : c;
 #pragma unroll
-      for (int i = 0; i < kBlockElems; ++i) {
+      for (int i = 0; i < 64; ++i) {
         const float p = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[i]), 0xB1, 0xF, 0xF, false));
         v[i] = __builtin_fmaf(p, sgn, v[i]);
       }
     }
+    if constexpr (G == 256) {
+      // stage 128: the same half of blocks b (even) and b ^ 1, two lanes
+      // apart; both carry the same sign, so the odd block's RN(v - p)
+      // flips it
+      const bool odd = (b & 1) != 0;
+      const float sgn = odd ? -1.0f : 1.0f;
+      c = odd ? -c : c;
 #pragma unroll
-    for (int i = 0; i < kBlockElems; ++i) {
+      for (int i = 0; i < 64; ++i) {
+        const float p = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[i]), 0x4E, 0xF, 0xF, false));
+        v[i] = __builtin_fmaf(p, sgn, v[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
       v[i] = v[i] * c;
       amax = fmaxf(amax, fabsf(v[i]));
     }
-    atomicMax(&row_amax[lrow], __float_as_uint(amax));   // amax >= 0: bit order = value order
+    atomicMax(&row_amax[lrow], __float_as_uint(amax));
   }
   __syncthreads();
 
-  // codes -> LDS (block b's 8 code chunks at j ^ ((b >> 1) & 7)), then out
-  uint4* codes = tile;   // the input tile is no longer read
+  // codes -> LDS (block b's 8 code chunks at j ^ ((b >> 1) & 7); this lane
+  // writes chunks 4 * half .. 4 * half + 3), then out
+  uint4* codes = tile;
   if (active) {
     const float s = __uint_as_float(row_amax[lrow]) / 127.0f;
-    if (b % bpr == 0) scale[row0 + lrow] = s;
-    const float r = 1.0f / s;                      // correctly rounded reciprocal
+    if (b % bpr == 0 && half == 0) scale[row0 + lrow] = s;
+    const float r = 1.0f / s;
     char* out = reinterpret_cast<char*>(codes) + b * 128;
     if (r < 1e30f) {
-      // q1 = RN(v / s) exactly: q0 = RN(v r) is within one ulp of v/s, the
-      // fma gives the exact remainder v - q0 s, and one more fma with the
-      // correctly rounded reciprocal lands on the correctly rounded quotient
-      // (Markstein's division theorem; also checked against IEEE division
-      // on 3.9e8 random and near-tie operand pairs on the host).
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int jj = 0; jj < 4; ++jj) {
         uint32_t wd[4];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           uint32_t t[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float val = v[16 * j + 4 * d + e];
+            const float val = v[16 * jj + 4 * d + e];
             const float q0 = val * r;
             const float rem = __builtin_fmaf(-q0, s, val);
             const float q1 = __builtin_fmaf(rem, r, q0);
-            // |q1| <= 127 * (1 + 2^-23): |val| <= amax and s = RN(amax / 127)
-            // >= (amax / 127)(1 - 2^-24), so rne(q1) is already within
-            // [-127, 127].  Adding 1.5 * 2^23 rounds q1 to an integer, ties to
-            // even, in the adder, and leaves that integer in two's complement
-            // in the low mantissa bits: the code is the low byte.
             t[e] = __float_as_uint(q1 + 12582912.0f);
           }
-          // bytes 0 of t0..t3 -> one word (v_perm_b32 picks bytes of {a, b})
           const uint32_t lo = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0400u);
           const uint32_t hi = __builtin_amdgcn_perm(t[3], t[2], 0x0c0c0400u);
           wd[d] = lo | (hi << 16);
         }
-        reinterpret_cast<uint4*>(out)[j ^ ((b >> 1) & 7)] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        reinterpret_cast<uint4*>(out)[(4 * half + jj) ^ ((b >> 1) & 7)] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
       }
     } else {
-      // s == 0 (all-zero row: codes 0) or a scale too small for a normal
-      // reciprocal: plain division
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int jj = 0; jj < 4; ++jj) {
         uint32_t wd[4];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           uint32_t packed = 0;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            packed |= (static_cast<uint32_t>(quant_code(v[16 * j + 4 * d + e], s)) & 0xffu) << (8 * e);
+            packed |= (static_cast<uint32_t>(quant_code(v[16 * jj + 4 * d + e], s)) & 0xffu) << (8 * e);
           wd[d] = s != 0.0f ? packed : 0u;
         }
-        reinterpret_cast<uint4*>(out)[j ^ ((b >> 1) & 7)] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        reinterpret_cast<uint4*>(out)[(4 * half + jj) ^ ((b >> 1) & 7)] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
       }
     }
   }
-  // this wave stores its own blocks' codes (LDS operations of one wave
-  // complete in order, so its code writes above are visible to its reads)
+  // this wave stores its own 32 blocks' codes
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   uint4* dstq = reinterpret_cast<uint4*>(q + row0 * K);
   const int wcodes = wchunks / 2;
-  for (int c = 512 * wave + lane; c < 512 * wave + wcodes; c += 64) {
-    const int bb = c >> 3, j = c & 7;
-    dstq[c] = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(codes) + bb * 128)[j ^ ((bb >> 1) & 7)];
+  for (int cc = 256 * wave + lane; cc < 256 * wave + wcodes; cc += 64) {
+    const int bb = cc >> 3, j = cc & 7;
+    dstq[cc] = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(codes) + bb * 128)[j ^ ((bb >> 1) & 7)];
   }
 }
 
@@ -512,19 +505,24 @@ hipError_t rotate_quant_16(const In16* x, int64_t M, int64_t K, int group, int8_
   // only a handful of waves; the row kernel spreads a row over 256 lanes
   // instead (16 x 4096: 4.1 us instead of 7.0; 512 x 3072: 4.8 instead of 6.3).
   if (K <= kMaxBlockK && M * K > kSmallBatchElems) {
-    // Rows per workgroup: as many as fit (one block per thread), but no more
+    // Rows per workgroup: as many as fit (256 blocks, 512 lanes), but no more
     // than an even share of two workgroups per CU, so that every CU gets the
     // same work when the batch is small (M = 4608, K = 3072: 512 workgroups of
-    // 9 rows instead of 461 of 10, of which 205 CUs would run two).
+    // 9 rows instead of 461 of 10, of which 205 CUs would run two).  Two lanes
+    // per block, threads rounded up to whole waves; LDS holds 256 bytes per
+    // block, sized at launch (K = 12288: 48 KB, three workgroups per CU).
     const int fit = kMaxBlocksPerWg / static_cast<int>(K / kBlockElems);
     const int64_t share = (M + 2 * num_cus() - 1) / (2 * num_cus());
     const int rows_per_wg = static_cast<int>(share < fit ? share : fit);
     const int64_t wgs = (M + rows_per_wg - 1) / rows_per_wg;
+    const int blocks = rows_per_wg * static_cast<int>(K / kBlockElems);
+    const int threads = (2 * blocks + 63) / 64 * 64;
+    const size_t lds = static_cast<size_t>(blocks) * 256;
     if (group == 128)
-      hipLaunchKernelGGL((rotq_block_kernel<128, In16>), dim3(static_cast<uint32_t>(wgs)), dim3(256), 0,
+      hipLaunchKernelGGL((rotq_block_kernel<128, In16>), dim3(static_cast<uint32_t>(wgs)), dim3(threads), lds,
                          stream, x, M, static_cast<int>(K), rows_per_wg, q, scale);
     else
-      hipLaunchKernelGGL((rotq_block_kernel<256, In16>), dim3(static_cast<uint32_t>(wgs)), dim3(256), 0,
+      hipLaunchKernelGGL((rotq_block_kernel<256, In16>), dim3(static_cast<uint32_t>(wgs)), dim3(threads), lds,
                          stream, x, M, static_cast<int>(K), rows_per_wg, q, scale);
     return hipGetLastError();
   }
