@@ -44,9 +44,10 @@ def rand_bf16(M, K, seed, outliers=4, factor=20.0):
 
 # ---------------------------------------------------------------- rotate + quant
 
-# Batches of up to 2^21 elements take the row kernel (a row spread over 256
-# lanes), larger ones with K <= 32768 the block kernel (one lane per 128
-# elements, several rows per workgroup), K > 32768 the row kernel in two passes.
+# Batches of up to 2^21 elements with K < 8192 take the row kernel (a row
+# spread over 256 lanes); larger batches, or K >= 8192, with K <= 32768 the
+# block kernel (two lanes per 128 elements, several rows per workgroup);
+# K > 32768 the row kernel in two passes.
 ROTQ_CASES = [
     (5, 128, 128), (131, 512, 128), (300, 3072, 128), (77, 3072, 256), (40, 4096, 128),
     (33, 12288, 128), (20, 12288, 256), (9, 16384, 128), (7, 24576, 256), (3, 131072, 128),

@@ -38,7 +38,7 @@ def act(M, K, seed, io):
     return f16_bits(x) if io == "f16" else synth.to_bf16_bits(x)
 
 
-# the row kernel (M*K <= 2^21) and the block kernel
+# the row kernel (M*K <= 2^21, K < 8192) and the block kernel
 @pytest.mark.parametrize("M,K,g", [(37, 3072, 128), (701, 3072, 128), (523, 4096, 256), (9, 16384, 256)])
 def test_rotate_quant_f16_bit_exact(M, K, g):
     x = act(M, K, M + K, "f16")

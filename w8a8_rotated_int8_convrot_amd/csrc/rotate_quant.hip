@@ -500,11 +500,14 @@ template <typename In16>
 hipError_t rotate_quant_16(const In16* x, int64_t M, int64_t K, int group, int8_t* q,
                            float* scale, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  // Small batches (up to 2^21 elements, e.g. 512 x 4096): one lane per
-  // 128-element block leaves each lane a long serial chain of arithmetic and
-  // only a handful of waves; the row kernel spreads a row over 256 lanes
-  // instead (16 x 4096: 4.1 us instead of 7.0; 512 x 3072: 4.8 instead of 6.3).
-  if (K <= kMaxBlockK && M * K > kSmallBatchElems) {
+  // Small batches (up to 2^21 elements, e.g. 512 x 4096) with rows shorter
+  // than 8192: the token-block kernel has only a handful of waves there, and
+  // the row kernel, which spreads a row over 256 lanes, is faster (16 x 4096:
+  // 4.1 us instead of 5.4; 256 x 3072: 4.2 instead of 5.4).  From K = 8192 on
+  // a row kernel lane holds four or more chunks in a serial chain, and the
+  // block kernel wins at any batch (16 x 12288: 5.7 us instead of 8.1;
+  // 16 x 16384, rotated twice by the row kernel: 5.8 instead of 16.1).
+  if (K <= kMaxBlockK && (M * K > kSmallBatchElems || K >= 8192)) {
     // Rows per workgroup: as many as fit (256 blocks, 512 lanes), but no more
     // than an even share of two workgroups per CU, so that every CU gets the
     // same work when the batch is small (M = 4608, K = 3072: 512 workgroups of
