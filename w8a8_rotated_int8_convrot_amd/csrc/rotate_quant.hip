@@ -535,15 +535,15 @@ hipError_t rotate_quant_16(const In16* x, int64_t M, int64_t K, int group, int8_
 }  // namespace
 
 int num_cus() {
-  static int n = 0;
-  if (n == 0) {
+  // read once (thread-safe static initialisation), from the device current
+  // at the first call
+  static const int n = [] {
     int dev = 0, v = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
-  }
+      return v;
+    return 256;
+  }();
   return n;
 }
 
