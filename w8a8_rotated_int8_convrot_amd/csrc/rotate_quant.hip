@@ -325,7 +325,15 @@ __global__ __launch_bounds__(512) void rotq_block_kernel(
       v[i] = v[i] * c;
       amax = fmaxf(amax, fabsf(v[i]));
     }
-    atomicMax(&row_amax[lrow], __float_as_uint(amax));
+    // one LDS atomic per block, or per two blocks when rows hold an even
+    // number of blocks (a block pair then never straddles two rows): the
+    // atomics of one row all hit one LDS word and are served one at a time
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0xB1, 0xF, 0xF, false)));
+    const bool pairs = (bpr & 1) == 0;
+    if (pairs)
+      amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0x4E, 0xF, 0xF, false)));
+    if ((tid & (pairs ? 3 : 1)) == 0)
+      atomicMax(&row_amax[lrow], __float_as_uint(amax));   // amax >= 0: bit order = value order
   }
   __syncthreads();
 
