@@ -400,76 +400,99 @@ __global__ void zero_word_kernel(uint32_t* p) { *p = 0u; }
 // unpacking their weights): every row is dequantized (s * q in fp32) and
 // rotated back by R, which is its own inverse (symmetric and orthogonal), so
 // the same butterfly in the same order applies; the result is rounded to
-// bf16 or fp16.  One workgroup per row, the row streamed in segments of
-// 256 * 8 * CPT values (no pass over the whole row is needed).
-template <int G, int CPT, bool OutF16>
-__global__ __launch_bounds__(kThreads) void unpack_rows_kernel(
-    const int8_t* __restrict__ wq, int64_t K, const float* __restrict__ w_scale, int row_scale,
+// bf16 or fp16.  Two lanes per 128-element block, as in the token-block
+// kernel: lane 2b + h dequantizes and rotates elements [64h, 64h + 64) of
+// block b (blocks counted over the whole row-major weight), stages 1..32 in
+// the lane, stage 64 by one DPP exchange, stage 128 (g = 256) with the same
+// half of block b ^ 1.  Both lanes of an exchange run RN(own * sgn + partner),
+// sgn = +1 where a + b is kept and -1 where the lane holds b and keeps a - b,
+// so every value, zeros' signs included, is the sequential butterfly's.  No
+// LDS and no barrier: every lane reads 64 contiguous codes and writes 128
+// contiguous bytes (12288 x 3072: 30-33 us like the one-row-per-workgroup
+// kernel it replaced at g = 128, 30 instead of 35 us at g = 256).
+template <int G, bool OutF16>
+__global__ __launch_bounds__(256) void unpack_block_kernel(
+    const int8_t* __restrict__ wq, int64_t nblk, int bpr, const float* __restrict__ w_scale, int row_scale,
     uint16_t* __restrict__ out) {
-  constexpr int kSegment = kThreads * 8 * CPT;
-  const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int lane_in_group = tid % (G / 8);
-  const float s = w_scale[row_scale ? row : 0];
-  const int8_t* qr = wq + row * K;
-  uint16_t* orow = out + row * K;
-  float v[CPT][8];
-  for (int64_t base = 0; base < K; base += kSegment) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t b = t >> 1;
+  const int half = static_cast<int>(t & 1);
+  // whole blocks (and, for g = 256, whole block pairs: rows hold an even
+  // number of blocks) leave together, so every exchange partner is active
+  if (b >= nblk) return;
+  const float s = w_scale[row_scale ? b / bpr : 0];
+  const uint4* src = reinterpret_cast<const uint4*>(wq + b * 128 + 64 * half);
+  float v[64];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int64_t e = base + (static_cast<int64_t>(j) * kThreads + tid) * 8;
-      if (e < K) {
-        const uint2 w = *reinterpret_cast<const uint2*>(qr + e);
+  for (int c = 0; c < 4; ++c) {
+    const uint4 w = src[c];
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[j][i] = s * static_cast<float>(static_cast<int8_t>(w.x >> (8 * i)));
-          v[j][4 + i] = s * static_cast<float>(static_cast<int8_t>(w.y >> (8 * i)));
-        }
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[16 * c + 4 * k + i] = s * static_cast<float>(static_cast<int8_t>(wd[k] >> (8 * i)));
+  }
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], d = v[i + h];
+        v[i] = a + d;
+        v[i + h] = a - d;
       }
     }
+  }
+  {  // stage 64: the lower lane keeps RN(a + b), the upper RN(a - b)
+    const float sgn = half ? -1.0f : 1.0f;
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int64_t e = base + (static_cast<int64_t>(j) * kThreads + tid) * 8;
-      if (e < K) {
-        rotate_chunk<G>(v[j], lane_in_group);
-        if constexpr (OutF16) {
-          // round the fp32 value to fp16: keep it in fp32 here, or the
-          // compiler fuses the last multiply and the conversion into one
-          // mixed-precision instruction that rounds the exact product once
-#pragma unroll
-          for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(v[j][i]));
-        }
-        uint32_t p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint16_t lo, hi;
-          if constexpr (OutF16) {
-            lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[j][2 * i]));
-            hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[j][2 * i + 1]));
-          } else {
-            lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[j][2 * i]));
-            hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[j][2 * i + 1]));
-          }
-          p[i] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
-        }
-        *reinterpret_cast<uint4*>(orow + e) = make_uint4(p[0], p[1], p[2], p[3]);
-      }
+    for (int i = 0; i < 64; ++i) {
+      const float p = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[i]), 0xB1, 0xF, 0xF, false));
+      v[i] = __builtin_fmaf(v[i], sgn, p);
     }
+  }
+  if constexpr (G == 256) {  // stage 128: block b (even) keeps RN(a + b), b ^ 1 RN(a - b)
+    const float sgn = (b & 1) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const float p = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[i]), 0x4E, 0xF, 0xF, false));
+      v[i] = __builtin_fmaf(v[i], sgn, p);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    v[i] = v[i] * RotScale<G>::value;
+    // fp16 output: keep the product in fp32 (no fused multiply + conversion)
+    if constexpr (OutF16) asm volatile("" : "+v"(v[i]));
+  }
+  uint4* dst = reinterpret_cast<uint4*>(out + b * 128 + 64 * half);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t lo, hi;
+      if constexpr (OutF16) {
+        lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[8 * j + 2 * i]));
+        hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[8 * j + 2 * i + 1]));
+      } else {
+        lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[8 * j + 2 * i]));
+        hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[8 * j + 2 * i + 1]));
+      }
+      p[i] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+    }
+    dst[j] = make_uint4(p[0], p[1], p[2], p[3]);
   }
 }
 
 template <int G, bool OutF16>
 hipError_t launch_unpack_g(const int8_t* wq, const float* w_scale, bool row_scale, int64_t N, int64_t K,
                            uint16_t* out, hipStream_t stream) {
-  const int64_t slots = (K + kThreads * 8 - 1) / (kThreads * 8);
-  const dim3 grid(static_cast<uint32_t>(N)), block(kThreads);
-  const int rs = row_scale ? 1 : 0;
-  if (slots <= 1)
-    hipLaunchKernelGGL((unpack_rows_kernel<G, 1, OutF16>), grid, block, 0, stream, wq, K, w_scale, rs, out);
-  else if (slots <= 2)
-    hipLaunchKernelGGL((unpack_rows_kernel<G, 2, OutF16>), grid, block, 0, stream, wq, K, w_scale, rs, out);
-  else
-    hipLaunchKernelGGL((unpack_rows_kernel<G, 4, OutF16>), grid, block, 0, stream, wq, K, w_scale, rs, out);
+  const int64_t nblk = N * (K / 128);
+  const int64_t wgs = (2 * nblk + 255) / 256;
+  hipLaunchKernelGGL((unpack_block_kernel<G, OutF16>), dim3(static_cast<uint32_t>(wgs)), dim3(256), 0, stream, wq,
+                     nblk, static_cast<int>(K / 128), w_scale, row_scale ? 1 : 0, out);
   return hipGetLastError();
 }
 
