@@ -219,7 +219,12 @@ __global__ __launch_bounds__(kThreads) void rotate_rows_kernel(
 // (lanes two apart).  A lane that must keep a - b while it holds b computes
 // RN(b - a) = -RN(a - b) with the same fma its partner uses for RN(a + b) and
 // carries the sign into the final multiply (rounding to nearest is
-// symmetric), so every add is the one the sequential butterfly does.  With
+// symmetric), so every add is the one the sequential butterfly does and the
+// values match it up to the sign of an exact zero (a = b gives +0 where the
+// butterfly has +0 too, turned into -0 by the negated constant), which neither
+// the row maximum nor the code can see.  (The weight unpacking below, whose
+// output is the values themselves, uses RN(own * sgn + partner) instead.)
+// With
 // 64 values per lane a wave needs about 94 registers, so twice as many waves
 // share a SIMD as with a whole block per lane (4608 x 3072: 13.2 -> 11.7 us;
 // 4608 x 12288: 43.5 -> 36.8 us; identical codes and scales).  The codes go
