@@ -325,3 +325,42 @@ def test_rotate_quant_exact_ties(B, reps):
     assert np.array_equal(q.cpu().numpy(), q_ref) and np.array_equal(s.cpu().numpy(), s_ref)
     assert [int(q_ref[i, 7]) for i in range(len(halves))] == [2, 2, -4, 62, -126, 0]
     assert all(int(q_ref[i, 9]) == 0 for i in range(len(halves)))
+
+
+# Seeded random shapes over every automatic tile choice (few tokens with many
+# or few channels, 128 x 128 / 64 x 128 for small layers, 384 x 192 with and
+# without its half-height tail, 256 x 256), ragged in M and N: int32 products
+# bit-exact, the dequant epilogue bit-exact on the oracle's int32.
+def _random_shapes(n, seed):
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        band = i % 4
+        if band == 0:
+            M, N = int(r.integers(1, 17)), int(r.integers(1, 13000))
+        elif band == 1:
+            M, N = int(r.integers(17, 129)), int(r.integers(1, 13000))
+        elif band == 2:
+            M, N = int(r.integers(129, 1200)), int(r.integers(1, 4000))
+        else:
+            M, N = int(r.integers(1200, 3000)), int(r.integers(6000, 13000))
+        K = 128 * int(r.integers(1, 2 if M * N > 8e6 else 5 if M * N > 4e6 else 17))
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_shapes(16, 2026))
+def test_random_shapes_bit_exact(B, M, N, K):
+    a = rand_i8((M, K), M * 7 + K)
+    b = rand_i8((N, K), N * 5 + K)
+    r = np.random.default_rng(M + N)
+    s_x = (r.random(M) * 0.2 + 1e-3).astype(np.float32)
+    s_w = np.float32(1.7e-4)
+    bias = synth.to_bf16_bits(r.standard_normal(N) * 0.01)
+    ad, bd = torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)
+    acc = B.convrot_gemm_i32(ad, bd).cpu().numpy()
+    y = B.convrot_gemm_dequant(ad, torch.from_numpy(s_x).to(DEV), bd, torch.tensor([s_w], device=DEV),
+                               to_dev_bf16(bias, DEV))
+    acc_ref = oracle.gemm_i32(a, b)
+    assert np.array_equal(acc, acc_ref)
+    assert np.all(same_bf16(bits_of(y), oracle.epilogue(acc_ref, s_x, s_w, bias)))
