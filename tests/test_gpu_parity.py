@@ -364,3 +364,25 @@ def test_random_shapes_bit_exact(B, M, N, K):
     acc_ref = oracle.gemm_i32(a, b)
     assert np.array_equal(acc, acc_ref)
     assert np.all(same_bf16(bits_of(y), oracle.epilogue(acc_ref, s_x, s_w, bias)))
+
+
+def _random_rotq(n, seed):
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        g = 128 if i % 3 else 256
+        K = g * int(r.integers(1, 32768 // g + 1)) if i % 4 else g * int(r.integers(1, 8))
+        M = int(r.integers(1, max(2, min(3000, (1 << 23) // K))))
+        out.append((M, K, g))
+    return out
+
+
+@pytest.mark.parametrize("M,K,g", _random_rotq(12, 77))
+def test_random_rotate_quant_bit_exact(B, M, K, g):
+    # seeded random batch shapes over both activation kernels (small batches
+    # with short rows on the row kernel, the rest on the token-block kernel)
+    x = rand_bf16(M, K, seed=M + K + g, outliers=min(4, K // 64))
+    q, s = B.convrot_rotate_quant(to_dev_bf16(x, DEV), g)
+    q_ref, s_ref = oracle.quant_act(x, g)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
