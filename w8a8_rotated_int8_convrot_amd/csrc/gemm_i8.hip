@@ -686,12 +686,12 @@ hipError_t launch_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
 
 // Tile choice: CONVROT_GEMM_TILE=big|big8|wide|wide128|mid|skinny|skinny16|half|m32|m64|m128
 // forces one (the result does not depend on it).  Otherwise: M <= 16 streams
-// the weight with the 16 x 16 tile and M <= 128 with the tiles above that
-// keep the batch in one token tile (or, with few channels, in tiles of 32
-// tokens); larger layers with fewer 384 x 192 tiles than half the CUs use
-// 128 x 128 or 64 x 128 tiles; else the cost of a large tile is the number of
-// rounds its tiles take over the 256 CUs times the work of one tile, and the
-// cheaper of 256x256 and 384x192 (with its half-height tail, below) wins.
+// the weight with the 16 x 16 tile, and M <= 256 with the small tile whose
+// slowest CU moves the fewest operand bytes; larger layers with fewer
+// 384 x 192 tiles than half the CUs use 384 x 96, 128 x 128 or 64 x 128
+// tiles; else the cost of a large tile is the number of rounds its tiles take
+// over the 256 CUs times the work of one tile, and the cheaper of 256x256 and
+// 384x192 (with its half-height tail, below) wins.
 int forced_tile() {
   const char* e = getenv("CONVROT_GEMM_TILE");
   if (e == nullptr) return 0;
@@ -739,19 +739,38 @@ int64_t wide_cost(int64_t M, int64_t N) {
 }
 
 int pick_tile(int64_t M, int64_t N) {
+  const int64_t kCUs = num_cus();
   if (M <= 16) return 7;
-  if (M <= 128) {
-    if ((N + 63) / 64 >= 96) return M <= 64 ? 11 : 12;
-    return M <= 64 ? 5 : 10;
+  if (M <= 256) {
+    // Weight-streaming layers.  The slowest CU runs ceil(tiles / CUs) tiles,
+    // each moving its BN weight rows and BM token rows per K byte; weight rows
+    // count twice (they come from HBM, token rows mostly from L2).  The
+    // candidate with the least such traffic wins, ties to the narrower tile.
+    // Against the best forced tile on 28 shapes (M = 16..256, N = 3072..12288,
+    // K = 3072, weight from HBM): 1.3 % slower on average and 9 % at worst,
+    // where a rule by channel count alone was 4 % and 34 %.
+    struct Cand { int t, bn, bm; };
+    constexpr Cand kCands[] = {{7, 16, 16}, {5, 32, 32}, {10, 64, 32}, {11, 64, 64}, {12, 64, 128}, {3, 128, 128}};
+    int best = 7;
+    int64_t best_cost = -1;
+    for (const Cand& c : kCands) {
+      const int64_t tiles = ((N + c.bn - 1) / c.bn) * ((M + c.bm - 1) / c.bm);
+      const int64_t cost = (tiles + kCUs - 1) / kCUs * (2 * c.bn + c.bm);
+      if (best_cost < 0 || cost < best_cost) best = c.t, best_cost = cost;
+    }
+    return best;
   }
   // Fewer 384 x 192 tiles than half the CUs: smaller tiles give more
-  // workgroups, 128 x 128 (two per CU), or 64 x 128 where even those would
-  // fill less than half the CUs (weight from HBM: 512 x 12288 x 4096 in 51 us
-  // instead of 59, 1536 x 3072 x 3072 in 31 instead of 38, 512 x 3072 x 12288
-  // in 52 instead of 73; from 128 large tiles on, 384 x 192 is faster again:
-  // 768 x 12288 x 4096 in 64 us against 76 with 128 x 128)
-  const int64_t kCUs = num_cus();
-  if (2 * ((M + 191) / 192) * ((N + 383) / 384) < kCUs)
+  // workgroups: 384 x 96 when they make one full round (more than 3/8 of the
+  // CUs' worth of large tiles: 3072 x 3072 x 3072 in 34.5 us instead of 40.4),
+  // else 128 x 128 (two per CU), or 64 x 128 where even those would fill less
+  // than half the CUs (weight from HBM: 512 x 12288 x 4096 in 51 us instead of
+  // 59, 512 x 3072 x 12288 in 52 instead of 73; from 128 large tiles on,
+  // 384 x 192 is faster again: 768 x 12288 x 4096 in 64 us against 76 with
+  // 128 x 128)
+  const int64_t wide = ((M + 191) / 192) * ((N + 383) / 384);
+  if (2 * wide <= kCUs && 8 * wide > 3 * kCUs) return 8;
+  if (2 * wide < kCUs)
     return 2 * ((M + 127) / 128) * ((N + 127) / 128) < kCUs ? 12 : 3;
   // the 256 x 256 tile (one wave per SIMD) wins only by a clear margin: it
   // was as fast or slower on every shape measured, also where its cost is
