@@ -231,10 +231,12 @@ def test_bit_identical_run_to_run(B):
 
 # few-token shapes on each automatic choice: 16 x 16 (M <= 16), 64 x 64 and
 # 64 x 128 (many channels), 32 x 32 and 64 x 32 (few channels, ragged N), and
-# past 128 tokens 64 x 128 on layers too small for larger tiles (N down to 1)
+# past 128 tokens 64 x 128 on layers too small for larger tiles (N down to 1),
+# and 384 x 96 where 384 x 192 tiles would fill 3/8 to 1/2 of the CUs
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (1, 3, 256), (2, 5, 128), (16, 12288, 4096), (63, 130, 512),
                                    (40, 12288, 1024), (100, 9216, 512), (64, 3072, 1536), (128, 3000, 384),
-                                   (100, 1, 128), (65, 7, 256), (129, 5, 128), (300, 1001, 384)])
+                                   (100, 1, 128), (65, 7, 256), (129, 5, 128), (300, 1001, 384),
+                                   (3072, 3000, 256)])
 def test_small_and_ragged_shapes(B, M, N, K):
     r = np.random.default_rng(M + N + K)
     xb = rand_bf16(M, K, M + K, outliers=0)
