@@ -52,6 +52,7 @@ ROTQ_CASES = [
     (5, 128, 128), (131, 512, 128), (300, 3072, 128), (77, 3072, 256), (40, 4096, 128),
     (33, 12288, 128), (20, 12288, 256), (9, 16384, 128), (7, 24576, 256), (3, 131072, 128),
     (701, 3072, 128), (523, 4096, 256), (171, 12288, 128), (129, 16384, 256), (67, 32768, 128),
+    (600, 12288, 128), (1024, 3072, 256),
 ]
 
 
