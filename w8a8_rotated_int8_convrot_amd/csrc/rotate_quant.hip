@@ -75,6 +75,31 @@ __device__ inline void load8(const float* p, float (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// v of lane (this lane ^ T).  Inside a 16-lane row DPP moves do it: xor 1
+// and xor 2 are quad permutations, xor 4 is the quad reversal (xor 3)
+// followed by the half-row mirror (xor 7), xor 8 is a rotation of the row by
+// 8; wider distances go through ds_bpermute.
+template <int T>
+__device__ inline float lane_xor(float v) {
+  const int b = __float_as_int(v);
+  if constexpr (T == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true));
+  else if constexpr (T == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true));
+  else if constexpr (T == 4)
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(b, 0x1B, 0xF, 0xF, true), 0x141, 0xF, 0xF, true));
+  else if constexpr (T == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, true));
+  else return __shfl_xor(v, T);
+}
+
+// One butterfly stage between lanes T apart: the lower element keeps
+// RN(a + b), the upper RN(a - b) (a = lower), each as RN(own * sgn + partner)
+// with sgn = -1 on the upper lane.
+template <int T>
+__device__ inline void lane_stage(float (&v)[8], int lane_in_group) {
+  const float sgn = (lane_in_group & T) != 0 ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], sgn, lane_xor<T>(v[i]));
+}
+
 // Butterfly of one 8-element chunk that is part of a g-group spread over g/8
 // lanes; `lane_in_group` is this lane's index inside the group.
 template <int G>
@@ -90,16 +115,11 @@ __device__ inline void rotate_chunk(float (&v)[8], int lane_in_group) {
       }
     }
   }
-#pragma unroll
-  for (int t = 1; t < G / 8; t <<= 1) {
-    const bool upper = (lane_in_group & t) != 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = __shfl_xor(v[i], t);
-      // lower element keeps a + b, upper element keeps a - b (a = lower)
-      v[i] = upper ? (p - v[i]) : (v[i] + p);
-    }
-  }
+  lane_stage<1>(v, lane_in_group);
+  lane_stage<2>(v, lane_in_group);
+  lane_stage<4>(v, lane_in_group);
+  lane_stage<8>(v, lane_in_group);
+  if constexpr (G == 256) lane_stage<16>(v, lane_in_group);
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = v[i] * RotScale<G>::value;
 }
@@ -121,11 +141,19 @@ __device__ inline uint2 pack8(const float (&v)[8], float s) {
   return make_uint2(lo, hi);
 }
 
-// Maximum over the workgroup (max is exact and order-free).
+// Maximum over the workgroup (max is exact and order-free): inside each
+// 16-lane row by DPP moves, over the four rows of a wave by lane reads, over
+// the waves through LDS.
 __device__ inline float block_max(float a) {
   __shared__ float part[kThreads / 64];
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+  a = fmaxf(a, lane_xor<1>(a));
+  a = fmaxf(a, lane_xor<2>(a));
+  a = fmaxf(a, lane_xor<4>(a));
+  a = fmaxf(a, lane_xor<8>(a));
+  a = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 0)),
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 16))),
+            fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 32)),
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 48))));
   const int wave = threadIdx.x / 64;
   if ((threadIdx.x & 63) == 0) part[wave] = a;
   __syncthreads();
@@ -539,7 +567,7 @@ hipError_t rotate_quant_16(const In16* x, int64_t M, int64_t K, int group, int8_
   // Small batches (up to 2^21 elements, e.g. 512 x 4096) with rows shorter
   // than 8192: the token-block kernel has only a handful of waves there, and
   // the row kernel, which spreads a row over 256 lanes, is faster (16 x 4096:
-  // 4.1 us instead of 5.4; 256 x 3072: 4.2 instead of 5.4).  From K = 8192 on
+  // 3.2 us instead of 5.4; 256 x 3072: 3.4 instead of 5.4).  From K = 8192 on
   // a row kernel lane holds four or more chunks in a serial chain, and the
   // block kernel wins at any batch (16 x 12288: 5.7 us instead of 8.1;
   // 16 x 16384, rotated twice by the row kernel: 5.8 instead of 16.1).
