@@ -53,6 +53,7 @@ ROTQ_CASES = [
     (33, 12288, 128), (20, 12288, 256), (9, 16384, 128), (7, 24576, 256), (3, 131072, 128),
     (701, 3072, 128), (523, 4096, 256), (171, 12288, 128), (129, 16384, 256), (67, 32768, 128),
     (600, 12288, 128), (1024, 3072, 256),
+    (3, 33024, 256), (2, 33280, 128),          # two-pass rows with a partial last segment
 ]
 
 
