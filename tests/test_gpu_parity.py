@@ -74,7 +74,7 @@ def test_rotate_quant_bit_exact(B, M, K, g):
 
 @pytest.mark.parametrize("N,K,g,dt", [(512, 512, 128, "f32"), (300, 3072, 256, "f32"),
                                       (1000, 384, 128, "bf16"), (7, 16384, 128, "f32"),
-                                      (33, 12288, 256, "bf16")])
+                                      (33, 12288, 256, "bf16"), (5, 13056, 256, "f32")])
 def test_prepare_weight_bit_exact(B, N, K, g, dt):
     r = np.random.default_rng(N + K)
     w = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
