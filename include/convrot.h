@@ -3,9 +3,10 @@
  * AMD MI355X (gfx950).
  *
  * What the layer computes (page "int8 Compute", InvokeAI docs, opening
- * section): the weight is an int8_tensorwise build (int8 values plus one
- * scale) quantized after a rotation; each call rotates its input with the
- * same rotation, quantizes it to int8 per token and multiplies int8 by int8.
+ * section): the weight is stored as int8 codes with one scale for the whole
+ * tensor, coded after a rotation; each call applies that same rotation to its
+ * activation, codes it as int8 with one scale per token, and multiplies the
+ * two code tensors on the integer matrix units.
  * The rotation is group-wise (same page, "What stays on the default path":
  * groups of 256 in every published build; the synthetic workloads here also
  * use 128) and is applied block after block along K (page "Explanation of
@@ -24,9 +25,9 @@
  *          an all-zero token or weight gets scale 0 and codes 0)
  *   acc = q_x . Wq^T in int32 (exact)
  *   y   = bf16_rne(fmaf((float)acc, s_x[m] * s_w, bias[n]))   (bias 0 if NULL)
- * Results are bit-identical from run to run and do not depend on how the
- * tokens are sliced or tiled (page "int8 Compute": each path is bit-identical
- * from run to run; streamed and resident runs give the same image).
+ * Repeated calls give the same bytes, whatever the slicing of the tokens or
+ * the tile shape (page "int8 Compute": both paths repeat their results
+ * exactly, and a streamed model's image equals the resident one's).
  *
  * Conventions for every entry point
  *   - All tensors are row-major and contiguous; bf16 values are raw 16-bit
@@ -106,9 +107,9 @@ int convrot_prepare_weight(const void *w, int w_dtype, int64_t N, int64_t K, int
 /* ---------------------------------------------------------------- forward */
 
 /* Workspace bytes convrot_linear needs: codes and scales of one slice of
- * min(M, 2N) tokens (page "int8 Compute", "Memory": the input is quantized in
- * slices of at most twice the output width, so the working memory never
- * exceeds the 2*N*K bytes of the unpacked bf16 weight). */
+ * min(M, 2N) tokens (page "int8 Compute", "Memory": the activation is coded
+ * a slice at a time, no slice taller than two output widths, which keeps the
+ * working memory within the 2*N*K bytes an unpacked bf16 weight takes). */
 size_t convrot_linear_workspace(int64_t M, int64_t K, int64_t N);
 
 /* The whole layer: y = dequant(rotate_quant(x) . Wq^T) + bias.
@@ -151,7 +152,7 @@ int convrot_gemm_dequant(const int8_t *xq, const float *x_scale,
 
 /* ---------------------------------------------------------------- variants
  * The layer in FP16 (page "int8 Compute", "What stays on the default path":
- * the kernels run in BF16 and FP16) and with one weight scale per output
+ * compute is offered in BF16 or FP16) and with one weight scale per output
  * channel (page "Explanation of INT8 ConvRot", format table: row-wise
  * scaling).  Same kernels and the same definitions as above, except:
  *   - io_dtype / x_dtype CONVROT_F16: the activation, the bias and the output
@@ -191,10 +192,10 @@ int convrot_linear_ex(const void *x, int io_dtype, int64_t M, int64_t K, const i
                       void *stream);
 
 /* ---------------------------------------------------------------- streamed weights
- * Page "int8 Compute", "Partially loaded models": a layer whose weight is
- * still in host RAM is copied to the GPU as int8 for each step (half the bytes
- * of the unpacked weight) and computed exactly like a resident one, and the
- * result is bit-identical.  convrot_linear_streamed runs a sequence of layers
+ * Page "int8 Compute", "Partially loaded models": when a layer's weight lives
+ * in host memory, the int8 codes (half the size of an unpacked bf16 weight)
+ * cross to the GPU on every step and the layer runs as it would with the
+ * weight resident, with no change in the result's bits.  convrot_linear_streamed runs a sequence of layers
  * whose int8 weights live in pinned host memory: each weight is copied into
  * one of two device slots on `copy_stream` while the previous layer computes
  * on `stream`, and each layer then runs exactly as convrot_linear on its slot
@@ -245,10 +246,10 @@ int convrot_linear_streamed(const convrot_stream_layer *layers, int n_layers,
  *     then y = rnd(x . Wu^T + bias), the product in the compute dtype with an
  *     fp32 accumulator on the bf16/fp16 matrix cores.  The activation is not
  *     rotated or quantized.
- *   - "When something goes wrong": the first result for each layer shape and
- *     token-count bucket is checked against the default path; if it does not
- *     match, or a kernel fails, one warning is logged and that GPU uses the
- *     default path until the process ends.
+ *   - "When something goes wrong": a new combination of layer shape and
+ *     batch-size bucket is verified once against the default path; on a
+ *     disagreement or a kernel error a single warning is written and the
+ *     device stays on the default path for the rest of the process.
  *   - "Memory": the default path reserves the unpacked weight (2*N*K bytes);
  *     the check keeps 256 rows of the layer's output from each path.
  *   - "Enabling": a line is logged once per GPU when the int8 path is first
@@ -291,7 +292,10 @@ size_t convrot_guarded_workspace(int64_t M, int64_t K, int64_t N);
  *   - On the first call for a bucket the default path is also run on
  *     R = min(M, 256) rows spread evenly over the batch (row_i =
  *     i * (M - 1) / (R - 1)), and the call waits for the stream to compare
- *     them: the int8 result matches when all its R rows are finite and
+ *     them: the int8 result matches when no value of its R rows is
+ *     non-finite where the default path's is not (or the reverse) -- the
+ *     same infinity on both, an output past the io type's range, agrees and
+ *     is left out of the norms -- and
  *     ||y_int8 - y_default||_F / ||y_default||_F <= tol over those rows
  *     (tol = 0.1 unless configured; the int8 layer differs from the default
  *     path by its activation quantization).  A match marks the bucket

@@ -20,7 +20,7 @@ arrays through ctypes.  The steps and their sources:
 * O6 dequantize with act_scale * weight_scale plus bias to bf16 -- page
   "int8 Compute", "What stays on the default path" (BF16 compute).
 * Variants: fp16 in place of bf16 for the activation, the bias and the output
-  (same page and section: the kernels run in BF16 and FP16), and one weight
+  (same page and section: compute is offered in BF16 or FP16), and one weight
   scale per output channel (page "Explanation of INT8 ConvRot", the format
   table's row-wise scaling).
 * Default path, against which the guarded layer checks its first result per

@@ -8,9 +8,10 @@
  * round-to-nearest-even, in the order written.
  *
  * Sources of each step:
- *  - page "int8 Compute" (InvokeAI docs), opening section: the layer rotates
- *    and quantizes its input to int8 per token and multiplies int8 by int8;
- *    weights are an int8_tensorwise build (int8 values + one scale).
+ *  - page "int8 Compute" (InvokeAI docs), opening section: the activation is
+ *    rotated and coded as int8 with one scale per token, the integer codes of
+ *    activation and weight are multiplied together, and the weight is stored
+ *    as int8 codes with one scale for the whole tensor.
  *  - same page, "What stays on the default path": rotation is done in
  *    groups (256 in every published build); without it one outlier channel
  *    sets the scale of a whole token.

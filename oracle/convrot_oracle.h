@@ -6,10 +6,10 @@
  * check and the CPU-baseline leg of the benchmark may load it.  It shares no
  * code, header, table or constant with the HIP library.
  *
- * Method (page "int8 Compute", InvokeAI docs, opening section): each ConvRot
- * layer rotates its input, quantizes it to int8 per token, and multiplies int8
- * by int8; the weight is an int8_tensorwise build (int8 values plus one
- * scale).  The rotation works in groups (same page, "What stays on the default
+ * Method (page "int8 Compute", InvokeAI docs, opening section): a ConvRot
+ * layer rotates its activation, codes it as int8 with one scale per token,
+ * and multiplies those codes with the weight's int8 codes, which carry one
+ * scale for the whole tensor.  The rotation works in groups (same page, "What stays on the default
  * path": published builds use groups of 256) and is the same orthogonal block
  * rotation on both operands, so x.W^T = (xR).(WR)^T (page "Explanation of INT8
  * ConvRot", section "What is INT8 ConvRot?": rotation applied group by group,
@@ -80,7 +80,7 @@ int oracle_quant_act(const uint16_t *x, int64_t M, int64_t K, int g,
                      int8_t *q, float *s, float *x_rot);
 
 /* O4 with fp16 input bits when io_f16 != 0 (page "int8 Compute", "What
- * stays on the default path": the kernels run in BF16 and FP16). */
+ * stays on the default path": compute is offered in BF16 or FP16). */
 int oracle_quant_act_ex(const uint16_t *x, int io_f16, int64_t M, int64_t K, int g,
                         int8_t *q, float *s, float *x_rot);
 

@@ -5,8 +5,9 @@
   (fake device addresses are passed: a call that got past its checks would
   touch them, so these tests also show that the checks come first);
 * the workspace contract of the page "int8 Compute", section "Memory": the
-  input is quantized in slices of at most twice the output width, so the
-  working memory stays within the 2*N*K bytes of an unpacked bf16 weight.
+  activation is coded a slice of tokens at a time, a slice holding no more
+  tokens than two output widths, which keeps the working memory inside the
+  2*N*K bytes that an unpacked bf16 weight would take.
 """
 import ctypes
 import os

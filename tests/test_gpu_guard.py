@@ -1,9 +1,9 @@
 """The default (dequantizing) path and the guarded layer on the GPU.
 
-Page "int8 Compute" (InvokeAI docs), "When something goes wrong": the first
-result for each layer shape and token-count bucket is checked against the
-default path; a mismatch or a failed kernel logs one warning, and that GPU
-then uses the default path until restart.
+Page "int8 Compute" (InvokeAI docs), "When something goes wrong": a new
+combination of layer shape and batch-size bucket is verified once against the
+default path; on a disagreement or a kernel error a single warning is
+written and the device stays on the default path for the rest of the run.
 
 * The unpacked weight (dequantize, rotate back, round) is integer-and-rounding
   work done in a pinned fp32 order: bit-exact against the oracle.
@@ -232,3 +232,28 @@ def test_checking_call_refuses_capture_then_graph_replays_after_it(guard):
         graph.replay()
         torch.cuda.synchronize()
         assert same(y, B.convrot_linear(x, wq, s_w, g, bias))
+
+
+def test_check_agrees_where_both_paths_overflow_fp16(guard):
+    # one output channel past the fp16 range on both paths: a constant
+    # activation of 100 (rotated exactly: one nonzero per group) against a
+    # constant weight row of 0.1 gives ~10240, plus a bias of 60000; the
+    # rounded output is +inf on the int8 layer and on the default path alike,
+    # which is agreement, not a mismatch.  Every other channel is finite.
+    M, N, K, g = 64, 256, 1024, 128
+    w = weight(N, K, 11)
+    w[5] = 0.1
+    wq, s_w = B.convrot_prepare_weight_ex(torch.from_numpy(w).to(DEV), g, scale_mode="tensor")
+    x = dev16(f16_bits(np.full((M, K), 100.0)), "f16")
+    b = np.random.default_rng(3).standard_normal(N) * 0.01
+    b[5] = 60000.0
+    bias = dev16(f16_bits(b), "f16")
+    y = B.convrot_linear_guarded(x, wq, s_w, g, bias)
+    y_int8 = B.convrot_linear_ex(x, wq, s_w, g, bias)
+    y_def = B.convrot_default_linear(x, wq, s_w, g, bias)
+    assert torch.isinf(y_int8[:, 5]).all() and torch.isinf(y_def[:, 5]).all()
+    assert torch.isfinite(y_int8[:, [c for c in range(N) if c != 5]]).all()
+    st = B.convrot_guard_query(0)
+    assert not st["fallback"] and st["checks_run"] == 1, st
+    assert 0.0 <= st["last_error"] < 0.05
+    assert same(y, y_int8)

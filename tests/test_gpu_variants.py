@@ -1,6 +1,6 @@
 """GPU parity of the layer's variants against the oracle: fp16 in place of
 bf16 for the activation, the bias and the output (page "int8 Compute", "What
-stays on the default path": the kernels run in BF16 and FP16), and one weight
+stays on the default path": compute is offered in BF16 or FP16), and one weight
 scale per output channel (page "Explanation of INT8 ConvRot", format table:
 row-wise scaling).  Integer work (codes, scales) is compared bit for bit, and
 so are the outputs: both sides round the same fp32 value once to fp16 / bf16.

@@ -410,7 +410,9 @@ def test_nrmse_gate_and_rotation_helps_outliers(golden_dir):
         y, _, _ = oracle.linear(L.x_bits, wq, s_w, g, L.bias_bits)
         errs[g] = oracle.nrmse(oracle.bf16_bits_to_f32(y), ref)
     assert errs[128] <= gate and errs[256] <= gate
-    # "without the rotation a single outlier channel sets the scale for a whole token"
+    # page "int8 Compute", "What stays on the default path": with no rotation
+    # the largest channel alone decides each token's scale, so the other
+    # channels get few levels and the error grows
     assert errs[128] < errs[1] and errs[256] < errs[1]
 
 

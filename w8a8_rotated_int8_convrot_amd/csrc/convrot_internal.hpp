@@ -76,7 +76,9 @@ hipError_t launch_gemm_default(const uint16_t* x, const uint16_t* wu, const uint
 hipError_t launch_gather_rows(const uint16_t* x, int64_t M, int64_t K, int R, uint16_t* xs,
                               hipStream_t stream);
 // Per sampled row i: partial[3i..3i+2] = {sum_n (a - b)^2, sum_n b^2, count of
-// non-finite a}, a = y[row_i][n] (negated when flip), b = ydef[i][n], in fp64.
+// mismatched non-finite values}, a = y[row_i][n] (negated when flip),
+// b = ydef[i][n], in fp64; where a and b are the same infinity the position
+// is left out of the sums, and where either is otherwise not finite it counts.
 hipError_t launch_compare_rows(const uint16_t* y, const uint16_t* ydef, bool f16, int64_t M, int64_t N,
                                int R, bool flip, double* partial, hipStream_t stream);
 // The sampled row i of R over M rows.

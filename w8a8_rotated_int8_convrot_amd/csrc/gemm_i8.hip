@@ -2,8 +2,8 @@
 // the fused dequant + bias epilogue of the ConvRot linear layer.
 //
 // What is computed (page "int8 Compute", InvokeAI docs, opening section: the
-// layer multiplies int8 by int8 on the int8 matrix units; "What stays on the
-// default path": outputs in BF16):
+// product of the two code tensors runs on the integer matrix units; "What
+// stays on the default path": outputs in BF16):
 //   acc[m][n] = sum_k xq[m][k] * wq[n][k]                 (int32, exact)
 //   y[m][n]   = bf16_rne(fmaf((float)acc, x_scale[m] * w_scale, bias[n]))
 //

@@ -1,10 +1,10 @@
 // rotate_quant.hip -- group-wise Walsh-Hadamard rotation + int8 quantization
 // for gfx950.
 //
-// What is computed (page "int8 Compute", InvokeAI docs, opening section: each
-// layer rotates and quantizes its input to int8 per token; the weight is an
-// int8_tensorwise build; rotation groups per "What stays on the default
-// path"):
+// What is computed (page "int8 Compute", InvokeAI docs, opening section: a
+// layer's activation is rotated, then given int8 codes with one scale per
+// token; its weight holds int8 codes with a single tensor scale; the rotation
+// works in groups, "What stays on the default path"):
 //   v      = x_row rotated block by block by H_g / sqrt(g)
 //   scale  = max |v| / 127  (per token for activations, one for a weight)
 //   code   = clamp(rne(v / scale), -127, 127), 0 where scale == 0
