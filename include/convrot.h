@@ -129,6 +129,27 @@ int convrot_linear(const void *x_bf16, int64_t M, int64_t K,
                    const void *bias_bf16, void *y_bf16,
                    void *workspace, size_t ws_bytes, void *stream);
 
+/* convrot_linear for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without a workspace.  The codes and scales of a slice
+ * live in a library-owned device array of CONVROT_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) per GPU, allocated when the library's code object is loaded on
+ * that GPU and held until the process ends; its address is looked up once
+ * per device.  The call allocates nothing and runs the same kernels as
+ * convrot_linear with that array as its workspace, so its slices hold
+ * S = min(M, 2N, CONVROT_NOALLOC_SCRATCH_BYTES / (K + 4) rounded down to a
+ * multiple of 16) tokens and the bytes written equal convrot_linear's.
+ * Errors are those of convrot_linear; a K whose minimum slice would not fit
+ * the array is CONVROT_EWORKSPACE (no K <= 131072 reaches it).  Calls on one
+ * GPU share its array: calls on one stream are ordered, but calls whose work
+ * overlaps on the GPU (different streams, or several host threads) race on
+ * it and must be serialised by the caller.  Nothing in the array needs to
+ * start at zero: every byte a slice reads, that slice has written. */
+#define CONVROT_NOALLOC_SCRATCH_BYTES (32u << 20)
+int convrot_linear_noalloc(const void *x_bf16, int64_t M, int64_t K,
+                           const int8_t *wq, const float *w_scale, int64_t N, int group,
+                           const void *bias_bf16, void *y_bf16, void *stream);
+
 /* ---------------------------------------------------------------- stages
  * The same kernels convrot_linear launches, exposed one by one. */
 

@@ -104,6 +104,17 @@ int main() {
   expect(convrot_linear_ex(A, CONVROT_F16, 4, 256, b8, f, 3, 10, 128, nullptr, Y, W, 1 << 20, nullptr),
          CONVROT_EUNSUPPORTED, "linear_ex: scale mode");
 
+  // the no-allocation layer
+  expect(convrot_linear_noalloc(A, 4, 256, b8, f, 10, 64, nullptr, Y, nullptr), CONVROT_EUNSUPPORTED,
+         "noalloc: group 64");
+  expect(convrot_linear_noalloc(A, 4, 200, b8, f, 10, 128, nullptr, Y, nullptr), CONVROT_EINVAL,
+         "noalloc: K % g");
+  expect(convrot_linear_noalloc(nullptr, 4, 256, b8, f, 10, 128, nullptr, Y, nullptr), CONVROT_EINVAL,
+         "noalloc: NULL x");
+  expect(convrot_linear_noalloc(A, 4, 256, b8, f, 10, 128, nullptr, MIS, nullptr), CONVROT_EALIGN,
+         "noalloc: misaligned y");
+  expect(convrot_linear_noalloc(A, 0, 256, b8, f, 10, 128, nullptr, Y, nullptr), CONVROT_OK, "noalloc: M = 0");
+
   // streamed weights
   if (convrot_stream_slot_bytes(nullptr, 0) != 0) ++g_failed;
   ++g_checks;

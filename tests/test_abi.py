@@ -105,6 +105,19 @@ def test_linear_argument_errors(lib):
     assert b"workspace" in lib.convrot_last_error()
 
 
+def test_noalloc_argument_errors(lib):
+    # refused before any HIP call, like convrot_linear (no workspace argument)
+    f = lib.convrot_linear_noalloc
+    assert f(A, 64, 512, A, A, 64, 64, None, A, None) == EUNSUPPORTED
+    assert f(A, 64, 500, A, A, 64, 128, None, A, None) == EINVAL
+    assert f(A, 64, 512, A, A, 0, 128, None, A, None) == EINVAL
+    assert f(None, 64, 512, A, A, 64, 128, None, A, None) == EINVAL
+    assert f(A + 8, 64, 512, A, A, 64, 128, None, A, None) == EALIGN
+    assert f(A, 64, 512, A, A, 64, 128, None, A + 2, None) == EALIGN
+    assert f(None, 0, 512, None, None, 64, 128, None, None, None) == OK
+    assert lib.convrot_last_error() == b""
+
+
 def test_empty_batch_needs_nothing(lib):
     assert call_linear(lib, M=0, x=None, y=None, ws=None, ws_bytes=0) == OK
     assert lib.convrot_last_error() == b""

@@ -34,6 +34,7 @@ SIGNATURES = {
     "convrot_prepare_weight": ([_P, _I, _I64, _I64, _I, _P, _P, _P, _SZ, _P], _I),
     "convrot_linear_workspace": ([_I64, _I64, _I64], _SZ),
     "convrot_linear": ([_P, _I64, _I64, _P, _P, _I64, _I, _P, _P, _P, _SZ, _P], _I),
+    "convrot_linear_noalloc": ([_P, _I64, _I64, _P, _P, _I64, _I, _P, _P, _P], _I),
     "convrot_rotate_quant": ([_P, _I64, _I64, _I, _P, _P, _P], _I),
     "convrot_gemm_i32": ([_P, _P, _I64, _I64, _I64, _P, _P], _I),
     "convrot_gemm_dequant": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _I),
@@ -235,6 +236,30 @@ def convrot_linear(x, wq, w_scale, group, bias=None, out=None, workspace=None) -
         raise ValueError("convrot_linear: output shape mismatch")
     _call("convrot_linear", _ptr(x), M, K, _ptr(wq), _ptr(w_scale), N, group, _ptr(bias), _ptr(y),
           _ptr(workspace), workspace.numel(), _stream(x))
+    return y
+
+
+def convrot_linear_noalloc(x, wq, w_scale, group, bias=None, out=None) -> torch.Tensor:
+    """convrot_linear without a workspace: the library keeps the slice's codes
+    and scales in its own device array (see include/convrot.h), so the call
+    allocates nothing when ``out`` is given."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(wq, torch.int8, "wq", 2)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("convrot_linear_noalloc: K mismatch")
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias", 1)
+        if bias.numel() != N:
+            raise ValueError("convrot_linear_noalloc: bias must have N elements")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need(y, torch.bfloat16, "out", 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("convrot_linear_noalloc: output shape mismatch")
+    _call("convrot_linear_noalloc", _ptr(x), M, K, _ptr(wq), _ptr(w_scale), N, group, _ptr(bias), _ptr(y),
+          _stream(x))
     return y
 
 

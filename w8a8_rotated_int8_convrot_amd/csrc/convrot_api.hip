@@ -234,6 +234,61 @@ size_t convrot_linear_workspace(int64_t M, int64_t K, int64_t N) {
   return round_up(static_cast<size_t>(S) * static_cast<size_t>(K), 256) + static_cast<size_t>(S) * 4;
 }
 
+}  // extern "C"
+
+// Device memory of convrot_linear_noalloc: the codes and scales of one slice.
+// In host code `scratch` names a host-side stand-in; its device address on
+// each GPU is looked up once (with that GPU current) and kept per device.
+static __device__ __align__(256) unsigned char scratch[CONVROT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;
+
+int scratch_of_current_device(const char* who, void** out) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return hip_status(e, who);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess)
+      return hip_status(e, who);
+    if (p == nullptr || !aligned16(p))
+      return fail(CONVROT_EHIP, "%s: scratch array of device %d at an unusable address", who, dev);
+    it = g_scratch_ptr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return CONVROT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int convrot_linear_noalloc(const void* x_bf16, int64_t M, int64_t K, const int8_t* wq,
+                           const float* w_scale, int64_t N, int group, const void* bias_bf16,
+                           void* y_bf16, void* stream) {
+  const char* who = "convrot_linear_noalloc";
+  // argument errors first, before any HIP call
+  if (int rc = check_group(group, K, who)) return rc;
+  if (int rc = check_mn(M, N, who)) return rc;
+  if (M == 0) return ok();
+  if (!x_bf16 || !wq || !w_scale || !y_bf16) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
+  if (!aligned16(x_bf16) || !aligned16(wq) || !aligned16(y_bf16))
+    return fail(CONVROT_EALIGN, "%s: x, wq and y must be 16-byte aligned", who);
+  const size_t cap = CONVROT_NOALLOC_SCRATCH_BYTES;
+  const int64_t need = std::min<int64_t>(std::min<int64_t>(M, 2 * N), 16);
+  if (slice_rows(M, K, N, cap) < need)
+    return fail(CONVROT_EWORKSPACE, "%s: a slice of %lld tokens of K=%lld does not fit the %zu-byte scratch array",
+                who, static_cast<long long>(need), static_cast<long long>(K), cap);
+  void* ws = nullptr;
+  if (int rc = scratch_of_current_device(who, &ws)) return rc;
+  return linear_impl(who, x_bf16, CONVROT_BF16, M, K, wq, w_scale, CONVROT_SCALE_TENSOR, N, group, bias_bf16,
+                     y_bf16, ws, cap, stream);
+}
+
 int convrot_rotate_quant(const void* x_bf16, int64_t M, int64_t K, int group, int8_t* xq,
                          float* x_scale, void* stream) {
   return rotate_quant_impl("convrot_rotate_quant", x_bf16, CONVROT_BF16, M, K, group, xq, x_scale,
