@@ -259,7 +259,7 @@ def test_empty_batch_is_a_no_op(B):
     assert y.shape == (0, 8)
 
 
-@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "half",
+@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "half", "p128", "phalf",
                                   "m32", "m64", "m128"])
 @pytest.mark.parametrize("M,N,K", [(300, 1001, 384), (513, 1000, 1024), (1111, 777, 640)])
 def test_every_gemm_tile_is_bit_exact(B, tile, M, N, K, monkeypatch):
@@ -278,6 +278,30 @@ def test_every_gemm_tile_is_bit_exact(B, tile, M, N, K, monkeypatch):
     acc_ref = oracle.gemm_i32(a, b)
     assert np.array_equal(acc, acc_ref)
     assert np.all(same_bf16(bits_of(y), oracle.epilogue(acc_ref, s_x, s_w, bias)))
+
+
+@pytest.mark.parametrize("M,N,K", [(2500, 9001, 384), (3001, 12288, 640), (4608, 9216, 3072), (5000, 12289, 1152)])
+def test_persistent_tiles_bit_exact(B, M, N, K, monkeypatch):
+    # the persistent 384 x 192 kernel with several tiles per workgroup (its
+    # pipeline crosses tile boundaries), ragged edges, 3 to 24 slabs of K; the
+    # 4608 x 9216 layer also runs its 384 x 96 tail; int32 and the bf16
+    # epilogue against the oracle on seeded rows, which include the edges
+    monkeypatch.setenv("CONVROT_GEMM_TILE", "p128")
+    a = rand_i8((M, K), 3 * M + K)
+    b = rand_i8((N, K), 5 * N + K)
+    r = np.random.default_rng(M + N + K)
+    s_x = (r.random(M) * 0.2 + 1e-3).astype(np.float32)
+    s_w = np.float32(1.1e-4)
+    bias = synth.to_bf16_bits(r.standard_normal(N) * 0.01)
+    ad, bd = torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)
+    acc = B.convrot_gemm_i32(ad, bd)
+    y = B.convrot_gemm_dequant(ad, torch.from_numpy(s_x).to(DEV), bd, torch.tensor([s_w], device=DEV),
+                               to_dev_bf16(bias, DEV))
+    rows = synth.sample_rows(M, 40, M * 3 + N)
+    ridx = torch.from_numpy(rows).to(DEV)
+    acc_ref = oracle.gemm_i32(a[rows], b)
+    assert np.array_equal(acc[ridx].cpu().numpy(), acc_ref)
+    assert np.all(same_bf16(bits_of(y[ridx]), oracle.epilogue(acc_ref, s_x[rows], s_w, bias)))
 
 
 @pytest.mark.parametrize("M", [2000, 2112])

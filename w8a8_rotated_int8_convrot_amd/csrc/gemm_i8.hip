@@ -671,6 +671,432 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
   }
 }
 
+// ---------------------------------------------------------------- persistent two-stage tiles
+//
+// One workgroup per CU walks its share of the tiles (the same XCD-aware order
+// as the one-tile-per-workgroup kernel) and keeps the operand pipeline running
+// across tile boundaries: the slab after next is issued at every slab
+// boundary, also when it belongs to the next tile, so a new tile finds its
+// first slab landed and its second in flight.  The epilogue needs no LDS and
+// no barrier: each wave converts its accumulators, exchanges halves between
+// lanes 32 apart (v_permlane32_swap) so that every lane holds eight
+// consecutive output channels of one token, and stores them as 16-byte
+// pieces; the wave then goes straight on to the next tile's first slab while
+// the stores drain, and the next slab boundary waits only for the loads
+// issued before those stores (vector memory counts complete in issue order).
+// Token scales, weight scales and bias of a tile are fetched into registers
+// when the tile starts (one or two values per thread) and parked in a
+// double-buffered LDS table at its last slab boundary.  Three or more slabs
+// per tile (K >= 384); MF = 32.
+template <class T, int EPI>
+__global__ __launch_bounds__(T::kThreads) void gemm_persist_kernel(
+    const int8_t* __restrict__ wq, const int8_t* __restrict__ xq, int M, int N, int K,
+    int tiles_n, int tiles_m, const float* __restrict__ x_scale,
+    const float* __restrict__ w_scale, const uint16_t* __restrict__ bias,
+    void* __restrict__ out) {
+  static_assert(T::kStages == 2 && T::BK == 128 && T::kKSteps % 2 == 0, "two 128-byte stages");
+  static_assert(T::MF == 32, "32x32 result blocks");
+  constexpr bool DEQUANT = EPI != kEpiI32;
+  constexpr bool kRowScale = EPI == kEpiBf16Row || EPI == kEpiF16Row;
+  constexpr bool kDefault = EPI == kEpiDefBf16 || EPI == kEpiDefF16;
+  constexpr bool kF16 = EPI == kEpiF16 || EPI == kEpiF16Row || EPI == kEpiDefF16;
+  constexpr int OP = EPI == kEpiDefBf16 ? kOpBf16 : EPI == kEpiDefF16 ? kOpF16 : kOpI8;
+  // parameter table: bias [BN], row scales [BN] (row mode), token factors [BM]
+  constexpr int kPBias = 0;
+  constexpr int kPWs = T::BN;
+  constexpr int kPAlpha = kRowScale ? 2 * T::BN : T::BN;
+  constexpr int kParams = DEQUANT ? kPAlpha + (kDefault ? 0 : T::BM) : 0;
+  constexpr int kParamPerThread = (kParams + T::kThreads - 1) / T::kThreads;
+  // 16-byte output pieces per wave and tile (interior tiles): TN x TM blocks
+  // of 32 x 32, each stored as two pieces per lane
+  constexpr int kStores = T::TN * T::TM * 2;
+  constexpr int kParamFloats = ((kParams > 0 ? kParams : 1) + 3) / 4 * 4;
+  __shared__ __attribute__((aligned(16))) char lds[T::kLdsBytes + 2 * kParamFloats * 4];
+  float* ptab0 = reinterpret_cast<float*>(lds + T::kLdsBytes);
+
+  const int total = tiles_n * tiles_m;
+  // this workgroup's tiles: its XCD's contiguous run of the tile order,
+  // every wgs-th one (wgs = workgroups on this XCD)
+  const int nb = gridDim.x;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int wgs = (nb >> 3) + (xcd < (nb & 7) ? 1 : 0);
+  const int run_len = total / 8 + (xcd < total % 8 ? 1 : 0);
+  const int run0 = xcd * (total / 8) + min(xcd, total % 8);
+  auto tile_of = [&](int i, int& tn, int& tm) -> bool {   // i-th tile of this workgroup
+    const int r = local + i * wgs;
+    if (r >= run_len) return false;
+    const int v = run0 + r;
+    const int per_group = T::kGroupM * tiles_n;
+    const int gid = v / per_group;
+    const int first_m = gid * T::kGroupM;
+    const int gsz = min(tiles_m - first_m, T::kGroupM);
+    const int in_group = v - gid * per_group;
+    tm = first_m + in_group % gsz;
+    tn = in_group / gsz;
+    return true;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave / T::WM, wm = wave % T::WM;
+  const int KT = K / T::BK;
+
+  // ---- load cursor: the tile whose slabs are being issued (base pointers
+  // and the byte offset of its last valid row in each operand, for clamping
+  // ragged edges) and the next slab index.  A row past the edge is read as
+  // the same chunk of the last valid row.
+  struct Cursor { const int8_t* a; const int8_t* b; uint32_t last_a, last_b; };
+  auto cursor_of = [&](int tn, int tm) {
+    const int n0 = tn * T::BN, m0 = tm * T::BM;
+    Cursor c;
+    c.a = wq + static_cast<int64_t>(n0) * K;
+    c.b = xq + static_cast<int64_t>(m0) * K;
+    c.last_a = static_cast<uint32_t>((min(N - n0, T::BN) - 1) * K);
+    c.last_b = static_cast<uint32_t>((min(M - m0, T::BM) - 1) * K);
+    return c;
+  };
+  // per-lane offsets of the cursor's tile, recomputed when the cursor moves
+  // to another tile (from an opaque copy of the lane id, so that nothing of
+  // it stays live through the main loop)
+  uint32_t off[T::kLoads];
+  auto aim = [&](const Cursor& c) {
+    int lane_a = lane;
+    asm volatile("" : "+v"(lane_a));
+#pragma unroll
+    for (int j = 0; j < T::kLoads; ++j) {
+      const bool is_a = j < T::kALoads;
+      const int i = is_a ? wave * T::kALoads + j : wave * T::kBLoads + (j - T::kALoads);
+      const int row = T::kRowsPerLoad * i + lane_a / T::kRowChunks;
+      const uint32_t c16 = static_cast<uint32_t>(((lane_a % T::kRowChunks) ^ swz<T::MF, T::BK>(row)) * 16);
+      off[j] = min(static_cast<uint32_t>(row * K) + c16, (is_a ? c.last_a : c.last_b) + c16);
+    }
+  };
+  Cursor cur_ld;
+  int ld_kt = 0;
+  // issue slab ld_kt of the cursor's tile into stage `stage` (no branches, so
+  // the loads stay in the scheduling region of the MFMAs they are interleaved
+  // with)
+  auto issue_loads = [&](int stage, auto jb_c, auto je_c) {   // loads [jb, je) of the slab
+    const int64_t k0 = static_cast<int64_t>(ld_kt) * T::BK;
+#pragma unroll
+    for (int j = decltype(jb_c)::value; j < decltype(je_c)::value; ++j) {
+      const bool is_a = j < T::kALoads;
+      const int i = is_a ? wave * T::kALoads + j : wave * T::kBLoads + (j - T::kALoads);
+      const int dst = stage * T::kStageBytes + (is_a ? 0 : T::BN * T::BK) + i * T::kRowsPerLoad * T::BK;
+      const int8_t* base = (is_a ? cur_ld.a : cur_ld.b) + k0;
+      asm volatile("" : "+v"(off[j]));
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off[j]), (lds_void_t*)(lds + dst), 16, 0, 0);
+    }
+  };
+  using JA_ = std::integral_constant<int, 0>;
+  using JE_ = std::integral_constant<int, T::kLoads>;
+
+  // ---- fragment reads (as in the one-tile kernel)
+  constexpr int kRowMask = T::MF - 1;
+  constexpr int kChunkShift = T::MF == 16 ? 4 : 5;
+  const int frow = lane & kRowMask;
+  int frag[T::kKSteps];
+#pragma unroll
+  for (int kk = 0; kk < T::kKSteps; ++kk) {
+    const int chunk = kk * (T::kUnitBytes / 16) + (lane >> kChunkShift);
+    frag[kk] = frow * T::BK + (((chunk ^ swz<T::MF, T::BK>(frow)) & (T::kRowChunks - 1)) << 4);
+  }
+  const int a_base = wn * T::kWaveN * T::BK;
+  const int b_base = T::BN * T::BK + wm * T::kWaveM * T::BK;
+  using acc_t = typename Acc<T::MF, OP>::type;
+  acc_t acc[T::TN][T::TM];
+  struct KFrag { v4i a[T::TN], b[T::TM]; };
+  auto read_unit = [&](int slab_stage, int kk, KFrag& f) {
+    const char* st = lds + slab_stage * T::kStageBytes;
+#pragma unroll
+    for (int t = 0; t < T::TM; ++t)
+      f.b[t] = *reinterpret_cast<const v4i*>(st + b_base + t * T::MF * T::BK + frag[kk]);
+#pragma unroll
+    for (int t = 0; t < T::TN; ++t)
+      f.a[t] = *reinterpret_cast<const v4i*>(st + a_base + t * T::MF * T::BK + frag[kk]);
+  };
+  auto compute_unit = [&](const KFrag& f) {
+#pragma unroll
+    for (int i = 0; i < T::TN; ++i)
+#pragma unroll
+      for (int j = 0; j < T::TM; ++j) acc[i][j] = mfma<T::MF, OP>(f.a[i], f.b[j], acc[i][j]);
+  };
+  constexpr int kUnitMfmas = T::TN * T::TM;
+  constexpr int kUnitReads = T::TN + T::TM;
+  auto order_unit = [&](auto loads_c) {   // MFMAs interleaved with this unit's loads, then its reads
+    constexpr int kV = decltype(loads_c)::value;
+    constexpr int kPairV = kV < kUnitMfmas ? kV : kUnitMfmas;
+    constexpr int kPairD = kUnitReads < kUnitMfmas - kPairV ? kUnitReads : kUnitMfmas - kPairV;
+#pragma unroll
+    for (int i = 0; i < kPairV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // VMEM (direct-to-LDS load)
+    }
+#pragma unroll
+    for (int i = 0; i < kPairD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+    }
+    if constexpr (kUnitMfmas > kPairV + kPairD)
+      __builtin_amdgcn_sched_group_barrier(0x008, kUnitMfmas - kPairV - kPairD, 0);
+    if constexpr (kV > kPairV) __builtin_amdgcn_sched_group_barrier(0x010, kV - kPairV, 0);
+    if constexpr (kUnitReads > kPairD) __builtin_amdgcn_sched_group_barrier(0x100, kUnitReads - kPairD, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto order_boundary = [&](auto reads_c) {
+    constexpr int kV = T::kLoads;
+    constexpr int kR = decltype(reads_c)::value ? kUnitReads : 0;
+    constexpr int kT = kR == 0 ? (kV < kUnitMfmas ? kV : kUnitMfmas)
+                     : kV < kR ? (kV < kUnitMfmas ? kV : kUnitMfmas) : (kR < kUnitMfmas ? kR : kUnitMfmas);
+#pragma unroll
+    for (int i = 0; i < kT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // VMEM (direct-to-LDS load)
+      if constexpr (kR > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+    }
+    if constexpr (kUnitMfmas > kT) __builtin_amdgcn_sched_group_barrier(0x008, kUnitMfmas - kT, 0);
+    if constexpr (kV > kT) __builtin_amdgcn_sched_group_barrier(0x010, kV - kT, 0);
+    if constexpr (kR > kT) __builtin_amdgcn_sched_group_barrier(0x100, kR - kT, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- a tile's epilogue parameters, one or two per thread, fetched when the
+  // tile starts and parked in the LDS table at its epilogue
+  float pv[kParamPerThread > 0 ? kParamPerThread : 1];
+  auto fetch_params = [&](int n0, int m0) {
+#pragma unroll
+    for (int r = 0; r < kParamPerThread; ++r) {
+      const int p = tid + r * T::kThreads;
+      float v = 0.0f;
+      if (p < kParams) {
+        if (p < kPWs) {
+          if (bias != nullptr) {
+            const uint16_t h = bias[min(n0 + p, N - 1)];
+            v = kF16 ? static_cast<float>(__builtin_bit_cast(_Float16, h)) : __uint_as_float(static_cast<uint32_t>(h) << 16);
+          }
+        } else if (p < kPAlpha) {
+          v = w_scale[min(n0 + (p - kPWs), N - 1)];
+        } else {
+          v = x_scale[min(m0 + (p - kPAlpha), M - 1)];
+          if constexpr (!kRowScale) v = v * *w_scale;
+        }
+      }
+      pv[r] = v;
+    }
+  };
+
+  // ---- the compute side: current tile (tn, tm), the next (ntn, ntm)
+  int tn, tm, ntn = 0, ntm = 0;
+  if (!tile_of(0, tn, tm)) return;
+  bool more = tile_of(1, ntn, ntm);
+  Cursor nxt_ld = more ? cursor_of(ntn, ntm) : cursor_of(tn, tm);
+  KFrag f0, f1;
+  int g = 0;   // slabs computed so far: the current slab's stage is g & 1
+
+  int ti_par = 0;
+  // One slab: all its units, then the slab boundary: wait until the next slab
+  // has landed everywhere and everyone is done with this stage, and refill
+  // it with the slab after next.  AFTER: a tile's first slab after an
+  // epilogue: the wait leaves that epilogue's kStores output stores in flight
+  // (they were issued after every load this boundary needs; vector memory
+  // counts complete in issue order).  SWITCH (kt = KT - 2): the slab after next is the
+  // next tile's first, so the cursor moves to the next tile (after the last
+  // tile it stays and re-fetches its own last slab into a stage nobody reads
+  // for results).  LAST: the tile's epilogue parameters go to their LDS table
+  // before the barrier, and the boundary reads the next tile's first unit.
+  auto slab = [&](auto after_c, auto switch_c, auto last_c) {
+    constexpr bool AFTER = decltype(after_c)::value;
+    constexpr bool SWITCH = decltype(switch_c)::value;
+    constexpr bool LAST = decltype(last_c)::value;
+    const int st = g & 1;
+    static_assert(T::kKSteps == 4, "four units per slab");
+    using L0_ = std::integral_constant<int, 0>;
+    read_unit(st, 1, f1);
+    compute_unit(f0);
+    order_unit(L0_{});
+    read_unit(st, 2, f0);
+    compute_unit(f1);
+    order_unit(L0_{});
+    read_unit(st, 3, f1);
+    compute_unit(f0);
+    order_unit(L0_{});
+    if constexpr (LAST && DEQUANT) {
+      float* pt = ptab0 + (ti_par & 1) * kParamFloats;
+#pragma unroll
+      for (int r = 0; r < kParamPerThread; ++r) {
+        const int p = tid + r * T::kThreads;
+        if (p < kParams) pt[p] = pv[r];
+      }
+    }
+    if constexpr (AFTER) wait_vm_barrier<kStores>();
+    else wait_vm_barrier<0>();
+    if constexpr (SWITCH) {
+      cur_ld = nxt_ld;
+      aim(cur_ld);
+      ld_kt = more ? 0 : KT - 1;
+    }
+    issue_loads(st, JA_{}, JE_{});
+    ld_kt = min(ld_kt + 1, KT - 1);
+    if constexpr (!LAST) read_unit(st ^ 1, 0, f0);
+    compute_unit(f1);
+    order_boundary(std::integral_constant<bool, !LAST>{});
+    ++g;
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+  // ---- prologue: the first tile's first two slabs
+  cur_ld = cursor_of(tn, tm);
+  aim(cur_ld);
+#pragma unroll
+  for (int i = 0; i < T::TN; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TM; ++j) acc[i][j] = acc_t{};
+  issue_loads(0, JA_{}, JE_{});
+  ld_kt = 1;
+  issue_loads(1, JA_{}, JE_{});
+  ld_kt = 2;
+  if constexpr (DEQUANT) fetch_params(tn * T::BN, tm * T::BM);
+  wait_vm_barrier<0>();   // slabs 0 and 1 have landed (the first boundary waits as after an epilogue)
+  read_unit(0, 0, f0);
+
+  for (int ti = 0;; ++ti) {
+    const int n0 = tn * T::BN, m0 = tm * T::BM;
+    ti_par = ti;
+    // slabs 0 .. KT-1: the first (after an epilogue, or the prologue), plain
+    // ones, the cursor's switch at KT - 2, the last
+    slab(T_{}, F_{}, F_{});
+    for (int kt = 1; kt + 2 < KT; ++kt) slab(F_{}, F_{}, F_{});
+    slab(F_{}, T_{}, F_{});
+    slab(F_{}, F_{}, T_{});
+    // ---- epilogue of tile (tn, tm), straight from registers: the last
+    // slab's boundary has published this tile's parameter table, and the
+    // next tile's first slab has landed in the other stage
+    int tid_e = tid;
+    asm volatile("" : "+v"(tid_e));   // epilogue addressing is not kept live through the loop
+    const int lane_e = tid_e & 63;
+    const int hi = lane_e >> 5;                         // lanes 32..63 hold channels 4..7 of each 8
+    const int n_loc = wn * T::kWaveN;
+    const int m_loc = wm * T::kWaveM + (lane_e & 31);
+    const bool whole = n0 + T::BN <= N && m0 + T::BM <= M;
+    if constexpr (DEQUANT) {
+      const float* pt = ptab0 + (ti_par & 1) * kParamFloats;
+      uint16_t* y = static_cast<uint16_t*>(out);
+      const bool vec = (N & 7) == 0;
+#pragma unroll
+      for (int j = 0; j < T::TM; ++j) {
+        const int m = m0 + m_loc + j * 32;
+        const float alpha = kDefault ? 0.0f : pt[kPAlpha + m_loc + j * 32];
+#pragma unroll
+        for (int i = 0; i < T::TN; ++i) {
+          uint32_t w[4][2];   // group g: channels 8g + 4*hi + (0..3), packed in pairs
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            const int nl = n_loc + i * 32 + 8 * gg + 4 * hi;
+            const float4 b4 = *reinterpret_cast<const float4*>(pt + kPBias + nl);
+            const float b[4] = {b4.x, b4.y, b4.z, b4.w};
+            float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+            if constexpr (kRowScale) {
+              const float4 s4 = *reinterpret_cast<const float4*>(pt + kPWs + nl);
+              sc[0] = s4.x; sc[1] = s4.y; sc[2] = s4.z; sc[3] = s4.w;
+            }
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if constexpr (kDefault) v[e] = acc[i][j][4 * gg + e] + b[e];
+              else if constexpr (kRowScale)
+                v[e] = __builtin_fmaf(static_cast<float>(acc[i][j][4 * gg + e]), alpha * sc[e], b[e]);
+              else v[e] = __builtin_fmaf(static_cast<float>(acc[i][j][4 * gg + e]), alpha, b[e]);
+            }
+            if constexpr (kF16) {
+              // fp16_rne of the fp32 result: no fused fma-and-convert
+#pragma unroll
+              for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(v[e]));
+              w[gg][0] = pack_f16x2(v[0], v[1]);
+              w[gg][1] = pack_f16x2(v[2], v[3]);
+            } else {
+              w[gg][0] = pack_bf16x2(v[0], v[1]);
+              w[gg][1] = pack_bf16x2(v[2], v[3]);
+            }
+          }
+          // groups (0,1) and (2,3): lanes l and l+32 trade halves, so lane
+          // l < 32 holds channels 16p + 0..7 and lane l + 32 channels 16p + 8..15
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            uint32_t q[4];
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+              const auto r = __builtin_amdgcn_permlane32_swap(w[2 * pp][d], w[2 * pp + 1][d], false, false);
+              q[d] = r[0];
+              q[2 + d] = r[1];
+            }
+            const uint4 piece = make_uint4(q[0], q[1], q[2], q[3]);
+            const int n = n0 + n_loc + i * 32 + 16 * pp + 8 * hi;
+            uint16_t* dstp = y + static_cast<int64_t>(m) * N + n;
+            if (whole) {
+              *reinterpret_cast<uint4*>(dstp) = piece;
+            } else if (m < M) {
+              if (vec && n + 8 <= N) {
+                *reinterpret_cast<uint4*>(dstp) = piece;
+              } else {
+                const uint32_t w4[4] = {piece.x, piece.y, piece.z, piece.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                  if (n + e < N) dstp[e] = static_cast<uint16_t>(w4[e >> 1] >> (16 * (e & 1)));
+              }
+            }
+          }
+        }
+      }
+    } else {
+      int32_t* c = static_cast<int32_t*>(out);
+      const bool vec = (N & 3) == 0;
+#pragma unroll
+      for (int i = 0; i < T::TN; ++i) {
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int n = n0 + n_loc + i * 32 + 8 * gg + 4 * hi;
+#pragma unroll
+          for (int j = 0; j < T::TM; ++j) {
+            const int m = m0 + m_loc + j * 32;
+            if (m >= M) continue;
+            int32_t* dstp = c + static_cast<int64_t>(m) * N + n;
+            const int a0 = acc[i][j][4 * gg], a1 = acc[i][j][4 * gg + 1];
+            const int a2 = acc[i][j][4 * gg + 2], a3 = acc[i][j][4 * gg + 3];
+            if (vec && n + 3 < N) {
+              *reinterpret_cast<int4*>(dstp) = make_int4(a0, a1, a2, a3);
+            } else {
+              if (n < N) dstp[0] = a0;
+              if (n + 1 < N) dstp[1] = a1;
+              if (n + 2 < N) dstp[2] = a2;
+              if (n + 3 < N) dstp[3] = a3;
+            }
+          }
+        }
+      }
+    }
+    // the next tile's first boundary leaves kStores stores in flight: that
+    // is exact for a whole tile's dequant epilogue; any other epilogue waits
+    // for its own stores here
+    if (!(DEQUANT && whole)) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (!more) break;
+#pragma unroll
+    for (int i = 0; i < T::TN; ++i)
+#pragma unroll
+      for (int j = 0; j < T::TM; ++j) acc[i][j] = acc_t{};
+    // ---- on to the next tile (its first slab landed, its second in
+    // flight): its parameters, the tile after it for the cursor, and its
+    // first unit
+    tn = ntn;
+    tm = ntm;
+    more = tile_of(ti + 2, ntn, ntm);
+    nxt_ld = more ? cursor_of(ntn, ntm) : cur_ld;
+    if constexpr (DEQUANT) fetch_params(tn * T::BN, tm * T::BM);
+    read_unit(g & 1, 0, f0);
+  }
+}
+
 template <class T, int EPI>
 hipError_t launch_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
                        const float* w_scale, const uint16_t* bias, void* out, int64_t M,
@@ -684,8 +1110,26 @@ hipError_t launch_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
   return hipGetLastError();
 }
 
-// Tile choice: CONVROT_GEMM_TILE=big|big8|wide|wide128|mid|skinny|skinny16|half|m32|m64|m128
-// forces one (the result does not depend on it).  Otherwise: M <= 16 streams
+// Persistent launch: one workgroup per CU (at most one per tile).
+template <class T, int EPI>
+hipError_t launch_persist(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                          const float* w_scale, const uint16_t* bias, void* out, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream) {
+  const int tiles_n = static_cast<int>((N + T::BN - 1) / T::BN);
+  const int tiles_m = static_cast<int>((M + T::BM - 1) / T::BM);
+  const int64_t tiles = static_cast<int64_t>(tiles_n) * tiles_m;
+  const int64_t grid = tiles < num_cus() ? tiles : num_cus();
+  if (K < 3 * T::BK) return launch_tile<T, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  hipLaunchKernelGGL((gemm_persist_kernel<T, EPI>), dim3(static_cast<uint32_t>(grid)), dim3(T::kThreads), 0,
+                     stream, wq, xq, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), tiles_n,
+                     tiles_m, x_scale, w_scale, bias, out);
+  return hipGetLastError();
+}
+
+// Tile choice: CONVROT_GEMM_TILE=big|big8|wide|wide128|mid|skinny|skinny16|half|m32|m64|m128|p128|phalf
+// forces one (the result does not depend on it; p128 and phalf are the
+// persistent 384 x 192 and 384 x 96 kernels, which take the one-tile kernel
+// below three slabs of K).  Otherwise: M <= 16 streams
 // the weight with the 16 x 16 tile, and M <= 256 with the small tile whose
 // slowest CU moves the fewest operand bytes; larger layers with fewer
 // 384 x 192 tiles than half the CUs use 384 x 96, 128 x 128 or 64 x 128
@@ -706,6 +1150,8 @@ int forced_tile() {
   if (strcmp(e, "m32") == 0) return 10;
   if (strcmp(e, "m64") == 0) return 11;
   if (strcmp(e, "m128") == 0) return 12;
+  if (strcmp(e, "p128") == 0) return 13;
+  if (strcmp(e, "phalf") == 0) return 14;
   return 0;
 }
 
@@ -785,11 +1231,19 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                        const float* w_scale, const uint16_t* bias, void* out, int64_t M,
                        int64_t N, int64_t K, hipStream_t stream) {
   int t = forced_tile();
-  if (t == 0) t = pick_tile(M, N);
+  const bool automatic = t == 0;
+  if (automatic) t = pick_tile(M, N);
   if (t == 1) return launch_tile<TileBig, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 2) return launch_tile<TileBig8, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 4) return launch_tile<TileWide, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 5) return launch_tile<TileSkinny, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (automatic && t == 6) {
+    // persistent 384 x 192 tiles where a workgroup gets several (more tiles
+    // than CUs) and K has three or more slabs, one-tile workgroups
+    // otherwise; both with the half-height tail below
+    const int64_t tiles = ((N + 383) / 384) * wide_main_m(M, N);
+    if (tiles > num_cus() && K >= 3 * 128) t = 13;
+  }
   if (t == 6) {
     // whole rounds of 384 x 192, then (if any) the rest of M as 384 x 96;
     // K counts bytes, and the output rows are 2 (dequant) or 4 (int32) bytes
@@ -803,6 +1257,17 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                           K, stream);
   }
   if (t == 8) return launch_tile<TileWideHalf, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 13) {
+    const int64_t split = wide_main_m(M, N) * 192;
+    if (split >= M) return launch_persist<TileWide128, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+    hipError_t e = launch_persist<TileWide128, EPI>(xq, x_scale, wq, w_scale, bias, out, split, N, K, stream);
+    if (e != hipSuccess) return e;
+    // the tail is at most one round: one tile per workgroup
+    const int64_t out_elem = EPI == kEpiI32 ? 4 : 2;
+    return launch_tile<TileWideHalf, EPI>(xq + split * K, x_scale ? x_scale + split : nullptr, wq, w_scale, bias,
+                                          static_cast<char*>(out) + split * N * out_elem, M - split, N, K, stream);
+  }
+  if (t == 14) return launch_persist<TileWideHalf, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 7) return launch_tile<TileSkinny16, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 10) return launch_tile<TileM32, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 11) return launch_tile<TileM64, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
