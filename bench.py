@@ -727,7 +727,7 @@ def main():
                        "value": round(2.0 * M * N * K / cold_s / 1e12, 2),
                        "note": "the first W warm-up + K timed steps of the run, before settling"},
         "rotate_quant_ms": round(rotq_ms, 5),
-        "roofline": {"bound": "mfma", "kernel": "gemm_i8_kernel (GEMM + dequant/bias epilogue)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_persist_kernel (persistent 384x192 GEMM + dequant/bias epilogue)",
                      "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                      "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
                      "gemm_ms": round(gemm_ms, 5)},

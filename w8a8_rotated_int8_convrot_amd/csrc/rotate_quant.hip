@@ -268,6 +268,35 @@ constexpr int kMaxBlocksPerWg = 256;                 // two lanes per block: 512
 constexpr int kMaxBlockK = kMaxBlocksPerWg * kBlockElems;
 constexpr int64_t kSmallBatchElems = int64_t{1} << 21;
 
+// v[i] <- RN(v[i] + sgn * v[i] of the partner lane) for all 64 values, one
+// v_fmac_f32 with a DPP source per value (the partner is the neighbour lane,
+// P = 0, or the lane two away, P = 1, inside each quad).  Eight values per
+// asm block; each block opens with the two wait states a DPP read needs after
+// a VALU write of its source (inside a block no instruction reads what another
+// of the block wrote).
+template <int P>
+__device__ inline void dpp_fmac8(float (&v)[64], float sgn) {
+#define CONVROT_DPP8(i0, PERM)                                                                          \
+  asm volatile("s_nop 1\n\t"                                                                            \
+               "v_fmac_f32_dpp %0, %0, %8 " PERM " row_mask:0xf bank_mask:0xf\n\t"                      \
+               "v_fmac_f32_dpp %1, %1, %8 " PERM " row_mask:0xf bank_mask:0xf\n\t"                      \
+               "v_fmac_f32_dpp %2, %2, %8 " PERM " row_mask:0xf bank_mask:0xf\n\t"                      \
+               "v_fmac_f32_dpp %3, %3, %8 " PERM " row_mask:0xf bank_mask:0xf\n\t"                      \
+               "v_fmac_f32_dpp %4, %4, %8 " PERM " row_mask:0xf bank_mask:0xf\n\t"                      \
+               "v_fmac_f32_dpp %5, %5, %8 " PERM " row_mask:0xf bank_mask:0xf\n\t"                      \
+               "v_fmac_f32_dpp %6, %6, %8 " PERM " row_mask:0xf bank_mask:0xf\n\t"                      \
+               "v_fmac_f32_dpp %7, %7, %8 " PERM " row_mask:0xf bank_mask:0xf"                            \
+               : "+v"(v[i0]), "+v"(v[i0 + 1]), "+v"(v[i0 + 2]), "+v"(v[i0 + 3]), "+v"(v[i0 + 4]),         \
+                 "+v"(v[i0 + 5]), "+v"(v[i0 + 6]), "+v"(v[i0 + 7])                                         \
+               : "v"(sgn))
+#pragma unroll
+  for (int i = 0; i < 64; i += 8) {
+    if constexpr (P == 0) CONVROT_DPP8(i, "quad_perm:[1,0,3,2]");
+    else CONVROT_DPP8(i, "quad_perm:[2,3,0,1]");
+  }
+#undef CONVROT_DPP8
+}
+
 template <int G, typename In16>
 __global__ __launch_bounds__(512) void rotq_block_kernel(
     const In16* __restrict__ x, int64_t M, int K, int rows_per_wg,
@@ -334,11 +363,7 @@ __global__ __launch_bounds__(512) void rotq_block_kernel(
     {  // stage 64: the lower half keeps RN(a + b), the upper RN(b - a)
       const float sgn = half ? -1.0f : 1.0f;
       c = half ? -c : c;
-#pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        const float p = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[i]), 0xB1, 0xF, 0xF, false));
-        v[i] = __builtin_fmaf(p, sgn, v[i]);
-      }
+      dpp_fmac8<0>(v, sgn);
     }
     if constexpr (G == 256) {
       // stage 128: the same half of blocks b (even) and b ^ 1, two lanes
@@ -347,11 +372,7 @@ __global__ __launch_bounds__(512) void rotq_block_kernel(
       const bool odd = (b & 1) != 0;
       const float sgn = odd ? -1.0f : 1.0f;
       c = odd ? -c : c;
-#pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        const float p = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[i]), 0x4E, 0xF, 0xF, false));
-        v[i] = __builtin_fmaf(p, sgn, v[i]);
-      }
+      dpp_fmac8<1>(v, sgn);
     }
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
