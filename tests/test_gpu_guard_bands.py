@@ -81,7 +81,7 @@ def gemm_case(B, M, N, K, seed):
     assert torch.equal(y.view(torch.int16, (M, N)), ref.view(torch.int16))
 
 
-@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "half", "p128", "phalf",
+@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "half", "p128", "phalf", "tall", "ptall",
                                   "m32", "m64", "m128"])
 @pytest.mark.parametrize("M,N,K", [(301, 1001, 384), (17, 35, 256), (1111, 777, 128)])
 def test_gemm_stores_stay_inside_on_every_tile(B, tile, M, N, K, monkeypatch):
@@ -89,11 +89,12 @@ def test_gemm_stores_stay_inside_on_every_tile(B, tile, M, N, K, monkeypatch):
     gemm_case(B, M, N, K, M + N + K)
 
 
+@pytest.mark.parametrize("tile", ["p128", "ptall"])
 @pytest.mark.parametrize("M,N,K", [(2500, 9001, 384), (4700, 12290, 640)])
-def test_gemm_stores_stay_inside_persistent_tiles(B, M, N, K, monkeypatch):
-    # more 384 x 192 tiles than CUs: each persistent workgroup runs several,
-    # ragged in both M and N
-    monkeypatch.setenv("CONVROT_GEMM_TILE", "p128")
+def test_gemm_stores_stay_inside_persistent_tiles(B, tile, M, N, K, monkeypatch):
+    # more tiles than CUs: each persistent workgroup runs several, ragged in
+    # both M and N
+    monkeypatch.setenv("CONVROT_GEMM_TILE", tile)
     gemm_case(B, M, N, K, 11 * M + N)
 
 

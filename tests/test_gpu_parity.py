@@ -259,7 +259,7 @@ def test_empty_batch_is_a_no_op(B):
     assert y.shape == (0, 8)
 
 
-@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "half", "p128", "phalf",
+@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "half", "p128", "phalf", "tall", "ptall",
                                   "m32", "m64", "m128"])
 @pytest.mark.parametrize("M,N,K", [(300, 1001, 384), (513, 1000, 1024), (1111, 777, 640)])
 def test_every_gemm_tile_is_bit_exact(B, tile, M, N, K, monkeypatch):
@@ -280,13 +280,16 @@ def test_every_gemm_tile_is_bit_exact(B, tile, M, N, K, monkeypatch):
     assert np.all(same_bf16(bits_of(y), oracle.epilogue(acc_ref, s_x, s_w, bias)))
 
 
-@pytest.mark.parametrize("M,N,K", [(2500, 9001, 384), (3001, 12288, 640), (4608, 9216, 3072), (5000, 12289, 1152)])
-def test_persistent_tiles_bit_exact(B, M, N, K, monkeypatch):
-    # the persistent 384 x 192 kernel with several tiles per workgroup (its
-    # pipeline crosses tile boundaries), ragged edges, 3 to 24 slabs of K; the
-    # 4608 x 9216 layer also runs its 384 x 96 tail; int32 and the bf16
-    # epilogue against the oracle on seeded rows, which include the edges
-    monkeypatch.setenv("CONVROT_GEMM_TILE", "p128")
+@pytest.mark.parametrize("tile", ["p128", "ptall"])
+@pytest.mark.parametrize("M,N,K", [(2500, 9001, 384), (3001, 12288, 640), (4608, 9216, 3072), (4608, 3072, 12288),
+                                   (5000, 12289, 1152)])
+def test_persistent_tiles_bit_exact(B, tile, M, N, K, monkeypatch):
+    # the persistent 384 x 192 and 192 x 288 kernels with several tiles per
+    # workgroup (the pipeline crosses tile boundaries), ragged edges, 3 to 24
+    # slabs of K; with p128 the 4608 x 9216 layer also runs its 384 x 96
+    # tail; int32 and the bf16 epilogue against the oracle on seeded rows,
+    # which include the edges
+    monkeypatch.setenv("CONVROT_GEMM_TILE", tile)
     a = rand_i8((M, K), 3 * M + K)
     b = rand_i8((N, K), 5 * N + K)
     r = np.random.default_rng(M + N + K)

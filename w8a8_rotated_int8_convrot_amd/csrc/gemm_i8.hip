@@ -144,6 +144,15 @@ using TileWide128 = Tile<384, 192, 4, 3, 32, 8, 2, 128>;
 // round (M = 4608, N = 9216: 504 tiles in two rounds, then 144 half tiles;
 // 163 us instead of 171 with 256 x 256 tiles over three rounds).
 using TileWideHalf = Tile<384, 96, 4, 3, 32, 4, 2, 128>;
+// 192 channels x 288 tokens, 12 waves (each 96 x 48 with 16x16x64 MFMAs,
+// three waves per SIMD), 128-byte slabs in two stages.  M = 4608 splits into
+// 16 token tiles of 288: N = 3072 gives 256 tiles, one full round, where the
+// 192 tiles of 384 x 192 leave a quarter of the CUs idle; N = 9216 gives 768,
+// three full rounds of three-quarter-size tiles, where 384 x 192 takes two
+// rounds and a half-height tail.  Each wave reads a third more LDS bytes per
+// MFMA than with 96 x 64 blocks of 32x32 tiles, so it is used only where it
+// saves rounds.
+using TileTall = Tile<192, 288, 2, 6, 16, 4, 2, 128>;
 // A few dozen tokens (16 < M <= 128), where streaming the weight is still most
 // of the cost.  With many output channels (N/64 >= 96), 64 channels per
 // workgroup and the whole batch in one token tile, so each weight row leaves
@@ -250,12 +259,12 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 
 // Byte offset of element (row m, column n) of the bf16 output tile staged in
 // LDS: rows of BN*2 bytes, 16-byte chunks XOR-swizzled by the low bits of the
-// row (at most 4 bits, so the XOR stays inside the row for rows of 4 chunks,
-// 8, or any multiple of 16).
+// row (as many bits, up to 4, as divide the row's chunk count, so the XOR
+// stays inside the row).
 template <class T>
 __device__ inline int out_lds_offset(int m, int n) {
   constexpr int kChunks = T::BN / 8;
-  constexpr int kMask = kChunks >= 16 ? 15 : kChunks - 1;
+  constexpr int kMask = kChunks % 16 == 0 ? 15 : kChunks % 8 == 0 ? 7 : kChunks % 4 == 0 ? 3 : kChunks - 1;
   static_assert(kChunks % (kMask + 1) == 0 && (kMask & (kMask + 1)) == 0, "chunk swizzle group");
   return m * (T::BN * 2) + (((n >> 3) ^ (m & kMask)) << 4) + ((n & 7) << 1);
 }
@@ -687,7 +696,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
 // Token scales, weight scales and bias of a tile are fetched into registers
 // when the tile starts (one or two values per thread) and parked in a
 // double-buffered LDS table at its last slab boundary.  Three or more slabs
-// per tile (K >= 384); MF = 32.
+// per tile (K >= 384).  With 16x16 result blocks a lane holds four channels
+// of one token; v_permlane16_swap between the blocks of two neighbouring
+// channel tiles gives every lane eight consecutive channels.
 template <class T, int EPI>
 __global__ __launch_bounds__(T::kThreads) void gemm_persist_kernel(
     const int8_t* __restrict__ wq, const int8_t* __restrict__ xq, int M, int N, int K,
@@ -695,7 +706,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_persist_kernel(
     const float* __restrict__ w_scale, const uint16_t* __restrict__ bias,
     void* __restrict__ out) {
   static_assert(T::kStages == 2 && T::BK == 128 && T::kKSteps % 2 == 0, "two 128-byte stages");
-  static_assert(T::MF == 32, "32x32 result blocks");
+  static_assert(T::MF == 32 || T::TN % 2 == 0, "16x16 result blocks are stored in pairs along n");
   constexpr bool DEQUANT = EPI != kEpiI32;
   constexpr bool kRowScale = EPI == kEpiBf16Row || EPI == kEpiF16Row;
   constexpr bool kDefault = EPI == kEpiDefBf16 || EPI == kEpiDefF16;
@@ -707,9 +718,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_persist_kernel(
   constexpr int kPAlpha = kRowScale ? 2 * T::BN : T::BN;
   constexpr int kParams = DEQUANT ? kPAlpha + (kDefault ? 0 : T::BM) : 0;
   constexpr int kParamPerThread = (kParams + T::kThreads - 1) / T::kThreads;
-  // 16-byte output pieces per wave and tile (interior tiles): TN x TM blocks
-  // of 32 x 32, each stored as two pieces per lane
-  constexpr int kStores = T::TN * T::TM * 2;
+  // 16-byte output pieces per lane and tile (interior tiles): two per 32 x 32
+  // block, one per pair of 16 x 16 blocks
+  constexpr int kStores = T::MF == 32 ? T::TN * T::TM * 2 : T::TN * T::TM / 2;
   constexpr int kParamFloats = ((kParams > 0 ? kParams : 1) + 3) / 4 * 4;
   __shared__ __attribute__((aligned(16))) char lds[T::kLdsBytes + 2 * kParamFloats * 4];
   float* ptab0 = reinterpret_cast<float*>(lds + T::kLdsBytes);
@@ -910,17 +921,19 @@ __global__ __launch_bounds__(T::kThreads) void gemm_persist_kernel(
     constexpr bool SWITCH = decltype(switch_c)::value;
     constexpr bool LAST = decltype(last_c)::value;
     const int st = g & 1;
-    static_assert(T::kKSteps == 4, "four units per slab");
+    static_assert(T::kKSteps == 4 || T::kKSteps == 2, "two or four units per slab");
     using L0_ = std::integral_constant<int, 0>;
     read_unit(st, 1, f1);
     compute_unit(f0);
     order_unit(L0_{});
-    read_unit(st, 2, f0);
-    compute_unit(f1);
-    order_unit(L0_{});
-    read_unit(st, 3, f1);
-    compute_unit(f0);
-    order_unit(L0_{});
+    if constexpr (T::kKSteps == 4) {
+      read_unit(st, 2, f0);
+      compute_unit(f1);
+      order_unit(L0_{});
+      read_unit(st, 3, f1);
+      compute_unit(f0);
+      order_unit(L0_{});
+    }
     if constexpr (LAST && DEQUANT) {
       float* pt = ptab0 + (ti_par & 1) * kParamFloats;
 #pragma unroll
@@ -976,104 +989,143 @@ __global__ __launch_bounds__(T::kThreads) void gemm_persist_kernel(
     int tid_e = tid;
     asm volatile("" : "+v"(tid_e));   // epilogue addressing is not kept live through the loop
     const int lane_e = tid_e & 63;
-    const int hi = lane_e >> 5;                         // lanes 32..63 hold channels 4..7 of each 8
     const int n_loc = wn * T::kWaveN;
-    const int m_loc = wm * T::kWaveM + (lane_e & 31);
     const bool whole = n0 + T::BN <= N && m0 + T::BM <= M;
-    if constexpr (DEQUANT) {
-      const float* pt = ptab0 + (ti_par & 1) * kParamFloats;
-      uint16_t* y = static_cast<uint16_t*>(out);
-      const bool vec = (N & 7) == 0;
+    // dequant + bias of four consecutive channels nl.. (tile-relative) of one
+    // token, packed in two words
+    auto dq4 = [&](const float* pt, float alpha, int nl, const auto& a, int e0, uint32_t (&w)[2]) {
+      const float4 b4 = *reinterpret_cast<const float4*>(pt + kPBias + nl);
+      const float b[4] = {b4.x, b4.y, b4.z, b4.w};
+      float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      if constexpr (kRowScale) {
+        const float4 s4 = *reinterpret_cast<const float4*>(pt + kPWs + nl);
+        sc[0] = s4.x; sc[1] = s4.y; sc[2] = s4.z; sc[3] = s4.w;
+      }
+      float v[4];
 #pragma unroll
-      for (int j = 0; j < T::TM; ++j) {
-        const int m = m0 + m_loc + j * 32;
-        const float alpha = kDefault ? 0.0f : pt[kPAlpha + m_loc + j * 32];
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (kDefault) v[e] = a[e0 + e] + b[e];
+        else if constexpr (kRowScale) v[e] = __builtin_fmaf(static_cast<float>(a[e0 + e]), alpha * sc[e], b[e]);
+        else v[e] = __builtin_fmaf(static_cast<float>(a[e0 + e]), alpha, b[e]);
+      }
+      if constexpr (kF16) {
+        // fp16_rne of the fp32 result: no fused fma-and-convert
 #pragma unroll
-        for (int i = 0; i < T::TN; ++i) {
-          uint32_t w[4][2];   // group g: channels 8g + 4*hi + (0..3), packed in pairs
+        for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(v[e]));
+        w[0] = pack_f16x2(v[0], v[1]);
+        w[1] = pack_f16x2(v[2], v[3]);
+      } else {
+        w[0] = pack_bf16x2(v[0], v[1]);
+        w[1] = pack_bf16x2(v[2], v[3]);
+      }
+    };
+    // eight consecutive output channels n.. of token m
+    auto put8 = [&](uint16_t* y, int m, int n, const uint4& piece, bool vec) {
+      uint16_t* dstp = y + static_cast<int64_t>(m) * N + n;
+      if (whole) {
+        *reinterpret_cast<uint4*>(dstp) = piece;
+      } else if (m < M) {
+        if (vec && n + 8 <= N) {
+          *reinterpret_cast<uint4*>(dstp) = piece;
+        } else {
+          const uint32_t w4[4] = {piece.x, piece.y, piece.z, piece.w};
 #pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            const int nl = n_loc + i * 32 + 8 * gg + 4 * hi;
-            const float4 b4 = *reinterpret_cast<const float4*>(pt + kPBias + nl);
-            const float b[4] = {b4.x, b4.y, b4.z, b4.w};
-            float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-            if constexpr (kRowScale) {
-              const float4 s4 = *reinterpret_cast<const float4*>(pt + kPWs + nl);
-              sc[0] = s4.x; sc[1] = s4.y; sc[2] = s4.z; sc[3] = s4.w;
-            }
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if constexpr (kDefault) v[e] = acc[i][j][4 * gg + e] + b[e];
-              else if constexpr (kRowScale)
-                v[e] = __builtin_fmaf(static_cast<float>(acc[i][j][4 * gg + e]), alpha * sc[e], b[e]);
-              else v[e] = __builtin_fmaf(static_cast<float>(acc[i][j][4 * gg + e]), alpha, b[e]);
-            }
-            if constexpr (kF16) {
-              // fp16_rne of the fp32 result: no fused fma-and-convert
-#pragma unroll
-              for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(v[e]));
-              w[gg][0] = pack_f16x2(v[0], v[1]);
-              w[gg][1] = pack_f16x2(v[2], v[3]);
-            } else {
-              w[gg][0] = pack_bf16x2(v[0], v[1]);
-              w[gg][1] = pack_bf16x2(v[2], v[3]);
-            }
-          }
-          // groups (0,1) and (2,3): lanes l and l+32 trade halves, so lane
-          // l < 32 holds channels 16p + 0..7 and lane l + 32 channels 16p + 8..15
-#pragma unroll
-          for (int pp = 0; pp < 2; ++pp) {
-            uint32_t q[4];
-#pragma unroll
-            for (int d = 0; d < 2; ++d) {
-              const auto r = __builtin_amdgcn_permlane32_swap(w[2 * pp][d], w[2 * pp + 1][d], false, false);
-              q[d] = r[0];
-              q[2 + d] = r[1];
-            }
-            const uint4 piece = make_uint4(q[0], q[1], q[2], q[3]);
-            const int n = n0 + n_loc + i * 32 + 16 * pp + 8 * hi;
-            uint16_t* dstp = y + static_cast<int64_t>(m) * N + n;
-            if (whole) {
-              *reinterpret_cast<uint4*>(dstp) = piece;
-            } else if (m < M) {
-              if (vec && n + 8 <= N) {
-                *reinterpret_cast<uint4*>(dstp) = piece;
-              } else {
-                const uint32_t w4[4] = {piece.x, piece.y, piece.z, piece.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                  if (n + e < N) dstp[e] = static_cast<uint16_t>(w4[e >> 1] >> (16 * (e & 1)));
-              }
-            }
-          }
+          for (int e = 0; e < 8; ++e)
+            if (n + e < N) dstp[e] = static_cast<uint16_t>(w4[e >> 1] >> (16 * (e & 1)));
         }
       }
-    } else {
-      int32_t* c = static_cast<int32_t*>(out);
-      const bool vec = (N & 3) == 0;
+    };
+    // four consecutive int32 results n.. of token m
+    auto put4i = [&](int32_t* c, int m, int n, int a0, int a1, int a2, int a3, bool vec) {
+      if (m >= M) return;
+      int32_t* dstp = c + static_cast<int64_t>(m) * N + n;
+      if (vec && n + 3 < N) {
+        *reinterpret_cast<int4*>(dstp) = make_int4(a0, a1, a2, a3);
+      } else {
+        if (n < N) dstp[0] = a0;
+        if (n + 1 < N) dstp[1] = a1;
+        if (n + 2 < N) dstp[2] = a2;
+        if (n + 3 < N) dstp[3] = a3;
+      }
+    };
+    if constexpr (T::MF == 32) {
+      const int hi = lane_e >> 5;                         // lanes 32..63 hold channels 4..7 of each 8
+      const int m_loc = wm * T::kWaveM + (lane_e & 31);
+      if constexpr (DEQUANT) {
+        const float* pt = ptab0 + (ti_par & 1) * kParamFloats;
+        uint16_t* y = static_cast<uint16_t*>(out);
+        const bool vec = (N & 7) == 0;
 #pragma unroll
-      for (int i = 0; i < T::TN; ++i) {
+        for (int j = 0; j < T::TM; ++j) {
+          const int m = m0 + m_loc + j * 32;
+          const float alpha = kDefault ? 0.0f : pt[kPAlpha + m_loc + j * 32];
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const int n = n0 + n_loc + i * 32 + 8 * gg + 4 * hi;
+          for (int i = 0; i < T::TN; ++i) {
+            uint32_t w[4][2];   // group g: channels 8g + 4*hi + (0..3), packed in pairs
 #pragma unroll
-          for (int j = 0; j < T::TM; ++j) {
-            const int m = m0 + m_loc + j * 32;
-            if (m >= M) continue;
-            int32_t* dstp = c + static_cast<int64_t>(m) * N + n;
-            const int a0 = acc[i][j][4 * gg], a1 = acc[i][j][4 * gg + 1];
-            const int a2 = acc[i][j][4 * gg + 2], a3 = acc[i][j][4 * gg + 3];
-            if (vec && n + 3 < N) {
-              *reinterpret_cast<int4*>(dstp) = make_int4(a0, a1, a2, a3);
-            } else {
-              if (n < N) dstp[0] = a0;
-              if (n + 1 < N) dstp[1] = a1;
-              if (n + 2 < N) dstp[2] = a2;
-              if (n + 3 < N) dstp[3] = a3;
+            for (int gg = 0; gg < 4; ++gg) dq4(pt, alpha, n_loc + i * 32 + 8 * gg + 4 * hi, acc[i][j], 4 * gg, w[gg]);
+            // groups (0,1) and (2,3): lanes l and l+32 trade halves, so lane
+            // l < 32 holds channels 16p + 0..7 and lane l + 32 channels 16p + 8..15
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+              uint32_t q[4];
+#pragma unroll
+              for (int d = 0; d < 2; ++d) {
+                const auto r = __builtin_amdgcn_permlane32_swap(w[2 * pp][d], w[2 * pp + 1][d], false, false);
+                q[d] = r[0];
+                q[2 + d] = r[1];
+              }
+              put8(y, m, n0 + n_loc + i * 32 + 16 * pp + 8 * hi, make_uint4(q[0], q[1], q[2], q[3]), vec);
             }
           }
         }
+      } else {
+        int32_t* c = static_cast<int32_t*>(out);
+        const bool vec = (N & 3) == 0;
+#pragma unroll
+        for (int i = 0; i < T::TN; ++i)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+            for (int j = 0; j < T::TM; ++j)
+              put4i(c, m0 + m_loc + j * 32, n0 + n_loc + i * 32 + 8 * gg + 4 * hi, acc[i][j][4 * gg],
+                    acc[i][j][4 * gg + 1], acc[i][j][4 * gg + 2], acc[i][j][4 * gg + 3], vec);
+      }
+    } else {
+      // 16 x 16 blocks: lane row r (16 lanes) holds channels 4r..4r+3 of
+      // token l % 16.  v_permlane16_swap of blocks X = (i, j) and Y = (i+1, j)
+      // trades rows 1 and 3 of X for rows 0 and 2 of Y, after which lane row
+      // r holds channels 8 (r >> 1) + 0..7 of X (r even) or of Y (r odd).
+      const int r16 = lane_e >> 4;
+      const int m_loc = wm * T::kWaveM + (lane_e & 15);
+      if constexpr (DEQUANT) {
+        const float* pt = ptab0 + (ti_par & 1) * kParamFloats;
+        uint16_t* y = static_cast<uint16_t*>(out);
+        const bool vec = (N & 7) == 0;
+#pragma unroll
+        for (int j = 0; j < T::TM; ++j) {
+          const int m = m0 + m_loc + j * 16;
+          const float alpha = kDefault ? 0.0f : pt[kPAlpha + m_loc + j * 16];
+#pragma unroll
+          for (int ip = 0; ip < T::TN / 2; ++ip) {
+            uint32_t wx[2], wy[2];
+            dq4(pt, alpha, n_loc + (2 * ip) * 16 + 4 * r16, acc[2 * ip][j], 0, wx);
+            dq4(pt, alpha, n_loc + (2 * ip + 1) * 16 + 4 * r16, acc[2 * ip + 1][j], 0, wy);
+            const auto p0 = __builtin_amdgcn_permlane16_swap(wx[0], wy[0], false, false);
+            const auto p1 = __builtin_amdgcn_permlane16_swap(wx[1], wy[1], false, false);
+            put8(y, m, n0 + n_loc + 16 * (2 * ip + (r16 & 1)) + 8 * (r16 >> 1),
+                 make_uint4(p0[0], p1[0], p0[1], p1[1]), vec);
+          }
+        }
+      } else {
+        int32_t* c = static_cast<int32_t*>(out);
+        const bool vec = (N & 3) == 0;
+#pragma unroll
+        for (int i = 0; i < T::TN; ++i)
+#pragma unroll
+          for (int j = 0; j < T::TM; ++j)
+            put4i(c, m0 + m_loc + j * 16, n0 + n_loc + i * 16 + 4 * r16, acc[i][j][0], acc[i][j][1],
+                  acc[i][j][2], acc[i][j][3], vec);
       }
     }
     // the next tile's first boundary leaves kStores stores in flight: that
@@ -1126,10 +1178,10 @@ hipError_t launch_persist(const int8_t* xq, const float* x_scale, const int8_t* 
   return hipGetLastError();
 }
 
-// Tile choice: CONVROT_GEMM_TILE=big|big8|wide|wide128|mid|skinny|skinny16|half|m32|m64|m128|p128|phalf
-// forces one (the result does not depend on it; p128 and phalf are the
-// persistent 384 x 192 and 384 x 96 kernels, which take the one-tile kernel
-// below three slabs of K).  Otherwise: M <= 16 streams
+// Tile choice: CONVROT_GEMM_TILE=big|big8|wide|wide128|mid|skinny|skinny16|half|m32|m64|m128|p128|phalf|tall|ptall
+// forces one (the result does not depend on it; p128, phalf and ptall are the
+// persistent 384 x 192, 384 x 96 and 192 x 288 kernels, which take the
+// one-tile kernel below three slabs of K).  Otherwise: M <= 16 streams
 // the weight with the 16 x 16 tile, and M <= 256 with the small tile whose
 // slowest CU moves the fewest operand bytes; larger layers with fewer
 // 384 x 192 tiles than half the CUs use 384 x 96, 128 x 128 or 64 x 128
@@ -1152,6 +1204,8 @@ int forced_tile() {
   if (strcmp(e, "m128") == 0) return 12;
   if (strcmp(e, "p128") == 0) return 13;
   if (strcmp(e, "phalf") == 0) return 14;
+  if (strcmp(e, "tall") == 0) return 15;
+  if (strcmp(e, "ptall") == 0) return 16;
   return 0;
 }
 
@@ -1218,6 +1272,10 @@ int pick_tile(int64_t M, int64_t N) {
   if (2 * wide <= kCUs && 8 * wide > 3 * kCUs) return 8;
   if (2 * wide < kCUs)
     return 2 * ((M + 127) / 128) * ((N + 127) / 128) < kCUs ? 12 : 3;
+  // 192 x 288 tiles where their rounds cost clearly less than those of
+  // 384 x 192 with its tail (a tenth less or more: they move more LDS bytes
+  // per MFMA); M = 4608: N = 3072 and 9216, not 12288
+  if (tile_cost(M, N, 192, 288) * 10 <= wide_cost(M, N) * 9) return 16;
   // the 256 x 256 tile (one wave per SIMD) wins only by a clear margin: it
   // was as fast or slower on every shape measured, also where its cost is
   // lower (M = 4608, N = 3072: 184 us for 216 tiles against 180 us for 192 at
@@ -1268,6 +1326,8 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                           static_cast<char*>(out) + split * N * out_elem, M - split, N, K, stream);
   }
   if (t == 14) return launch_persist<TileWideHalf, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 15) return launch_tile<TileTall, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 16) return launch_persist<TileTall, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 7) return launch_tile<TileSkinny16, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 10) return launch_tile<TileM32, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 11) return launch_tile<TileM64, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
