@@ -150,8 +150,8 @@ using TileWideHalf = Tile<384, 96, 4, 3, 32, 4, 2, 128>;
 // 192 tiles of 384 x 192 leave a quarter of the CUs idle; N = 9216 gives 768,
 // three full rounds of three-quarter-size tiles, where 384 x 192 takes two
 // rounds and a half-height tail.  Each wave reads a third more LDS bytes per
-// MFMA than with 96 x 64 blocks of 32x32 tiles, so it is used only where it
-// saves rounds.
+// MFMA than with 96 x 64 blocks of 32x32 tiles, but its epilogue hides better
+// behind the next tile's first MFMAs (18 per wave instead of 6).
 using TileTall = Tile<192, 288, 2, 6, 16, 4, 2, 128>;
 // A few dozen tokens (16 < M <= 128), where streaming the weight is still most
 // of the cost.  With many output channels (N/64 >= 96), 64 channels per
@@ -249,11 +249,15 @@ __device__ inline void tile_coords(int tiles_n, int tiles_m, int& tn, int& tm) {
   tn = in_group / gsz;
 }
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest even and packed, a in the low half: one
+// v_cvt_pk_bf16_f32 with both sources (converting the two values one by one
+// takes two conversions, a shift and an or).
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-  const __bf16 ha = static_cast<__bf16>(a);   // v_cvt_pk_bf16_f32: round to nearest even
-  const __bf16 hb = static_cast<__bf16>(b);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ha)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hb)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{a, b}), v2bf));
 }
 
 
@@ -275,11 +279,9 @@ __device__ inline int out_lds_offset(int m, int n) {
 enum Epi { kEpiI32 = 0, kEpiBf16 = 1, kEpiBf16Row = 2, kEpiF16 = 3, kEpiF16Row = 4,
            kEpiDefBf16 = 5, kEpiDefF16 = 6 };
 
+// The same for IEEE binary16 (v_cvt_pk_f16_f32, round to nearest even).
 __device__ inline uint32_t pack_f16x2(float a, float b) {
-  const _Float16 ha = static_cast<_Float16>(a);   // v_cvt_f16_f32: round to nearest even
-  const _Float16 hb = static_cast<_Float16>(b);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ha)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hb)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{a, b}), v2h));
 }
 __device__ inline float f16_bits_lo(uint32_t w) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
@@ -693,6 +695,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
 // pieces; the wave then goes straight on to the next tile's first slab while
 // the stores drain, and the next slab boundary waits only for the loads
 // issued before those stores (vector memory counts complete in issue order).
+// When the tile is whole and another follows, the next tile's first MFMA
+// unit runs inside the epilogue: each result block, once converted and
+// stored, restarts with that unit's MFMA, so the matrix cores are not idle
+// while the epilogue's vector work runs.
 // Token scales, weight scales and bias of a tile are fetched into registers
 // when the tile starts (one or two values per thread) and parked in a
 // double-buffered LDS table at its last slab boundary.  Three or more slabs
@@ -916,16 +922,19 @@ __global__ __launch_bounds__(T::kThreads) void gemm_persist_kernel(
   // tile it stays and re-fetches its own last slab into a stage nobody reads
   // for results).  LAST: the tile's epilogue parameters go to their LDS table
   // before the barrier, and the boundary reads the next tile's first unit.
-  auto slab = [&](auto after_c, auto switch_c, auto last_c) {
+  auto slab = [&](auto after_c, auto switch_c, auto last_c, auto skip0_c) {
     constexpr bool AFTER = decltype(after_c)::value;
     constexpr bool SWITCH = decltype(switch_c)::value;
     constexpr bool LAST = decltype(last_c)::value;
+    constexpr bool SKIP0 = decltype(skip0_c)::value;   // unit 0 ran inside the previous epilogue
     const int st = g & 1;
     static_assert(T::kKSteps == 4 || T::kKSteps == 2, "two or four units per slab");
     using L0_ = std::integral_constant<int, 0>;
     read_unit(st, 1, f1);
-    compute_unit(f0);
-    order_unit(L0_{});
+    if constexpr (!SKIP0) {
+      compute_unit(f0);
+      order_unit(L0_{});
+    }
     if constexpr (T::kKSteps == 4) {
       read_unit(st, 2, f0);
       compute_unit(f1);
@@ -973,16 +982,17 @@ __global__ __launch_bounds__(T::kThreads) void gemm_persist_kernel(
   if constexpr (DEQUANT) fetch_params(tn * T::BN, tm * T::BM);
   wait_vm_barrier<0>();   // slabs 0 and 1 have landed (the first boundary waits as after an epilogue)
   read_unit(0, 0, f0);
+  compute_unit(f0);
 
   for (int ti = 0;; ++ti) {
     const int n0 = tn * T::BN, m0 = tm * T::BM;
     ti_par = ti;
     // slabs 0 .. KT-1: the first (after an epilogue, or the prologue), plain
     // ones, the cursor's switch at KT - 2, the last
-    slab(T_{}, F_{}, F_{});
-    for (int kt = 1; kt + 2 < KT; ++kt) slab(F_{}, F_{}, F_{});
-    slab(F_{}, T_{}, F_{});
-    slab(F_{}, F_{}, T_{});
+    slab(T_{}, F_{}, F_{}, T_{});
+    for (int kt = 1; kt + 2 < KT; ++kt) slab(F_{}, F_{}, F_{}, F_{});
+    slab(F_{}, T_{}, F_{}, F_{});
+    slab(F_{}, F_{}, T_{}, F_{});
     // ---- epilogue of tile (tn, tm), straight from registers: the last
     // slab's boundary has published this tile's parameter table, and the
     // next tile's first slab has landed in the other stage
@@ -1048,95 +1058,94 @@ __global__ __launch_bounds__(T::kThreads) void gemm_persist_kernel(
         if (n + 3 < N) dstp[3] = a3;
       }
     };
-    if constexpr (T::MF == 32) {
-      const int hi = lane_e >> 5;                         // lanes 32..63 hold channels 4..7 of each 8
-      const int m_loc = wm * T::kWaveM + (lane_e & 31);
-      if constexpr (DEQUANT) {
-        const float* pt = ptab0 + (ti_par & 1) * kParamFloats;
-        uint16_t* y = static_cast<uint16_t*>(out);
-        const bool vec = (N & 7) == 0;
+    // Result block layout.  32 x 32: lanes 32..63 hold channels 4..7 of each
+    // 8.  16 x 16: lane row r (16 lanes) holds channels 4r..4r+3 of token
+    // l % 16; v_permlane16_swap of blocks X = (i, j) and Y = (i+1, j) trades
+    // rows 1 and 3 of X for rows 0 and 2 of Y, after which lane row r holds
+    // channels 8 (r >> 1) + 0..7 of X (r even) or of Y (r odd).
+    const int hi = T::MF == 32 ? lane_e >> 5 : lane_e >> 4;
+    const int m_loc = wm * T::kWaveM + (lane_e & (T::MF - 1));
+    const float* pt = ptab0 + (ti_par & 1) * kParamFloats;
+    // dequant epilogue of block (i, j) (32 x 32), or of blocks (i, j) and
+    // (i + 1, j) (16 x 16, i even)
+    auto epi_block = [&](int i, int j) {
+      uint16_t* y = static_cast<uint16_t*>(out);
+      const bool vec = (N & 7) == 0;
+      const int m = m0 + m_loc + j * T::MF;
+      const float alpha = kDefault ? 0.0f : pt[kPAlpha + m_loc + j * T::MF];
+      if constexpr (T::MF == 32) {
+        uint32_t w[4][2];   // group g: channels 8g + 4*hi + (0..3), packed in pairs
 #pragma unroll
-        for (int j = 0; j < T::TM; ++j) {
-          const int m = m0 + m_loc + j * 32;
-          const float alpha = kDefault ? 0.0f : pt[kPAlpha + m_loc + j * 32];
+        for (int gg = 0; gg < 4; ++gg) dq4(pt, alpha, n_loc + i * 32 + 8 * gg + 4 * hi, acc[i][j], 4 * gg, w[gg]);
+        // groups (0,1) and (2,3): lanes l and l+32 trade halves, so lane
+        // l < 32 holds channels 16p + 0..7 and lane l + 32 channels 16p + 8..15
 #pragma unroll
-          for (int i = 0; i < T::TN; ++i) {
-            uint32_t w[4][2];   // group g: channels 8g + 4*hi + (0..3), packed in pairs
+        for (int pp = 0; pp < 2; ++pp) {
+          uint32_t q[4];
 #pragma unroll
-            for (int gg = 0; gg < 4; ++gg) dq4(pt, alpha, n_loc + i * 32 + 8 * gg + 4 * hi, acc[i][j], 4 * gg, w[gg]);
-            // groups (0,1) and (2,3): lanes l and l+32 trade halves, so lane
-            // l < 32 holds channels 16p + 0..7 and lane l + 32 channels 16p + 8..15
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
-              uint32_t q[4];
-#pragma unroll
-              for (int d = 0; d < 2; ++d) {
-                const auto r = __builtin_amdgcn_permlane32_swap(w[2 * pp][d], w[2 * pp + 1][d], false, false);
-                q[d] = r[0];
-                q[2 + d] = r[1];
-              }
-              put8(y, m, n0 + n_loc + i * 32 + 16 * pp + 8 * hi, make_uint4(q[0], q[1], q[2], q[3]), vec);
-            }
+          for (int d = 0; d < 2; ++d) {
+            const auto r = __builtin_amdgcn_permlane32_swap(w[2 * pp][d], w[2 * pp + 1][d], false, false);
+            q[d] = r[0];
+            q[2 + d] = r[1];
           }
+          put8(y, m, n0 + n_loc + i * 32 + 16 * pp + 8 * hi, make_uint4(q[0], q[1], q[2], q[3]), vec);
         }
+      } else {
+        uint32_t wx[2], wy[2];
+        dq4(pt, alpha, n_loc + i * 16 + 4 * hi, acc[i][j], 0, wx);
+        dq4(pt, alpha, n_loc + (i + 1) * 16 + 4 * hi, acc[i + 1][j], 0, wy);
+        const auto p0 = __builtin_amdgcn_permlane16_swap(wx[0], wy[0], false, false);
+        const auto p1 = __builtin_amdgcn_permlane16_swap(wx[1], wy[1], false, false);
+        put8(y, m, n0 + n_loc + 16 * (i + (hi & 1)) + 8 * (hi >> 1), make_uint4(p0[0], p1[0], p0[1], p1[1]), vec);
+      }
+    };
+    constexpr int kIStep = T::MF == 32 ? 1 : 2;
+    // A whole tile's dequant epilogue with another tile to follow runs
+    // together with that tile's first unit: block by block, the results are
+    // converted and stored, and the block's accumulators restart with the
+    // next tile's first MFMA (whose fragments are read first: its slab has
+    // landed), so the matrix cores work through the epilogue.
+    const bool fuse = DEQUANT && whole && more;
+    if (fuse) {
+      read_unit(g & 1, 0, f0);
+#pragma unroll
+      for (int j = 0; j < T::TM; ++j)
+#pragma unroll
+        for (int i = 0; i < T::TN; i += kIStep) {
+          epi_block(i, j);
+#pragma unroll
+          for (int d = 0; d < kIStep; ++d) acc[i + d][j] = mfma<T::MF, OP>(f0.a[i + d], f0.b[j], acc_t{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+      if constexpr (DEQUANT) {
+#pragma unroll
+        for (int j = 0; j < T::TM; ++j)
+#pragma unroll
+          for (int i = 0; i < T::TN; i += kIStep) epi_block(i, j);
       } else {
         int32_t* c = static_cast<int32_t*>(out);
         const bool vec = (N & 3) == 0;
+        constexpr int kGroups = T::kAccRegs / 4;
 #pragma unroll
         for (int i = 0; i < T::TN; ++i)
 #pragma unroll
-          for (int gg = 0; gg < 4; ++gg)
+          for (int gg = 0; gg < kGroups; ++gg)
 #pragma unroll
             for (int j = 0; j < T::TM; ++j)
-              put4i(c, m0 + m_loc + j * 32, n0 + n_loc + i * 32 + 8 * gg + 4 * hi, acc[i][j][4 * gg],
+              put4i(c, m0 + m_loc + j * T::MF, n0 + n_loc + i * T::MF + 8 * gg + 4 * hi, acc[i][j][4 * gg],
                     acc[i][j][4 * gg + 1], acc[i][j][4 * gg + 2], acc[i][j][4 * gg + 3], vec);
       }
-    } else {
-      // 16 x 16 blocks: lane row r (16 lanes) holds channels 4r..4r+3 of
-      // token l % 16.  v_permlane16_swap of blocks X = (i, j) and Y = (i+1, j)
-      // trades rows 1 and 3 of X for rows 0 and 2 of Y, after which lane row
-      // r holds channels 8 (r >> 1) + 0..7 of X (r even) or of Y (r odd).
-      const int r16 = lane_e >> 4;
-      const int m_loc = wm * T::kWaveM + (lane_e & 15);
-      if constexpr (DEQUANT) {
-        const float* pt = ptab0 + (ti_par & 1) * kParamFloats;
-        uint16_t* y = static_cast<uint16_t*>(out);
-        const bool vec = (N & 7) == 0;
+      // the next tile's first boundary leaves kStores stores in flight: that
+      // is exact for a whole tile's dequant epilogue; any other epilogue
+      // waits for its own stores here
+      if (!(DEQUANT && whole)) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (!more) break;
 #pragma unroll
-        for (int j = 0; j < T::TM; ++j) {
-          const int m = m0 + m_loc + j * 16;
-          const float alpha = kDefault ? 0.0f : pt[kPAlpha + m_loc + j * 16];
+      for (int i = 0; i < T::TN; ++i)
 #pragma unroll
-          for (int ip = 0; ip < T::TN / 2; ++ip) {
-            uint32_t wx[2], wy[2];
-            dq4(pt, alpha, n_loc + (2 * ip) * 16 + 4 * r16, acc[2 * ip][j], 0, wx);
-            dq4(pt, alpha, n_loc + (2 * ip + 1) * 16 + 4 * r16, acc[2 * ip + 1][j], 0, wy);
-            const auto p0 = __builtin_amdgcn_permlane16_swap(wx[0], wy[0], false, false);
-            const auto p1 = __builtin_amdgcn_permlane16_swap(wx[1], wy[1], false, false);
-            put8(y, m, n0 + n_loc + 16 * (2 * ip + (r16 & 1)) + 8 * (r16 >> 1),
-                 make_uint4(p0[0], p1[0], p0[1], p1[1]), vec);
-          }
-        }
-      } else {
-        int32_t* c = static_cast<int32_t*>(out);
-        const bool vec = (N & 3) == 0;
-#pragma unroll
-        for (int i = 0; i < T::TN; ++i)
-#pragma unroll
-          for (int j = 0; j < T::TM; ++j)
-            put4i(c, m0 + m_loc + j * 16, n0 + n_loc + i * 16 + 4 * r16, acc[i][j][0], acc[i][j][1],
-                  acc[i][j][2], acc[i][j][3], vec);
-      }
+        for (int j = 0; j < T::TM; ++j) acc[i][j] = acc_t{};
     }
-    // the next tile's first boundary leaves kStores stores in flight: that
-    // is exact for a whole tile's dequant epilogue; any other epilogue waits
-    // for its own stores here
-    if (!(DEQUANT && whole)) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (!more) break;
-#pragma unroll
-    for (int i = 0; i < T::TN; ++i)
-#pragma unroll
-      for (int j = 0; j < T::TM; ++j) acc[i][j] = acc_t{};
     // ---- on to the next tile (its first slab landed, its second in
     // flight): its parameters, the tile after it for the cursor, and its
     // first unit
@@ -1145,7 +1154,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_persist_kernel(
     more = tile_of(ti + 2, ntn, ntm);
     nxt_ld = more ? cursor_of(ntn, ntm) : cur_ld;
     if constexpr (DEQUANT) fetch_params(tn * T::BN, tm * T::BM);
-    read_unit(g & 1, 0, f0);
+    if (!fuse) {
+      read_unit(g & 1, 0, f0);
+      compute_unit(f0);
+    }
   }
 }
 
@@ -1272,10 +1284,11 @@ int pick_tile(int64_t M, int64_t N) {
   if (2 * wide <= kCUs && 8 * wide > 3 * kCUs) return 8;
   if (2 * wide < kCUs)
     return 2 * ((M + 127) / 128) * ((N + 127) / 128) < kCUs ? 12 : 3;
-  // 192 x 288 tiles where their rounds cost clearly less than those of
-  // 384 x 192 with its tail (a tenth less or more: they move more LDS bytes
-  // per MFMA); M = 4608: N = 3072 and 9216, not 12288
-  if (tile_cost(M, N, 192, 288) * 10 <= wide_cost(M, N) * 9) return 16;
+  // 192 x 288 tiles where their rounds cost no more than those of 384 x 192
+  // with its tail: with the epilogue run beside the next tile's first MFMAs
+  // they are the faster of the two at equal cost (M = 4608, N = 12288,
+  // K = 3072: 140.4 us against 145.7; N = 3072 and 9216 take fewer rounds)
+  if (tile_cost(M, N, 192, 288) <= wide_cost(M, N)) return 16;
   // the 256 x 256 tile (one wave per SIMD) wins only by a clear margin: it
   // was as fast or slower on every shape measured, also where its cost is
   // lower (M = 4608, N = 3072: 184 us for 216 tiles against 180 us for 192 at
