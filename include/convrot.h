@@ -381,6 +381,18 @@ int convrot_guard_inject(int device, int fault);
 int convrot_probe_mfma_i8(const int8_t *a, int64_t a_bytes, const int8_t *b, int64_t b_bytes,
                           int blocks, int iters, int32_t *out, void *stream);
 
+/* A second measurement aid, also defined by no page: the traffic of
+ * rotate + quant without its arithmetic, so that a benchmark can state what
+ * this machine's HBM sustains for exactly that traffic.  Reads n 16-bit
+ * values from x_16 and writes the high byte of each to q[n] (q[i] =
+ * x_16[i] >> 8), 16-byte loads and 8-byte stores, grid-stride over at most
+ * 2048 workgroups.  x_16 and q are 16-byte aligned device buffers owned by
+ * the caller; asynchronous on `stream`; n = 0 is a no-op.
+ * Errors: n negative or not a multiple of 8, NULL buffer (n > 0) ->
+ * CONVROT_EINVAL; misalignment -> CONVROT_EALIGN; launch error ->
+ * CONVROT_EHIP. */
+int convrot_probe_stream(const void *x_16, int64_t n, int8_t *q, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -164,11 +164,14 @@ int main() {
   expect(convrot_guard_reset(-2), CONVROT_EINVAL, "guard reset: device");
   expect(convrot_guard_reset(0), CONVROT_OK, "guard reset");
 
-  // measurement aid
+  // measurement aids
   expect(convrot_probe_mfma_i8(a8, 4096, b8, 4096, 0, 1, (int32_t*)Y, nullptr), CONVROT_EINVAL,
          "probe: blocks 0");
   expect(convrot_probe_mfma_i8(a8, 8, b8, 4096, 1, 1, (int32_t*)Y, nullptr), CONVROT_EINVAL,
          "probe: short operand");
+  expect(convrot_probe_stream(A, 12, static_cast<int8_t*>(Y), nullptr), CONVROT_EINVAL,
+         "stream probe: n not a multiple of 8");
+  expect(convrot_probe_stream(nullptr, 8, static_cast<int8_t*>(Y), nullptr), CONVROT_EINVAL, "stream probe: NULL x");
 
   if (g_failed) {
     std::printf("abi_driver: %d of %d checks failed\n", g_failed, g_checks);

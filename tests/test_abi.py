@@ -165,6 +165,16 @@ def test_mfma_probe_argument_errors(lib):
     assert b"aligned" in lib.convrot_last_error()
 
 
+def test_stream_probe_argument_errors(lib):
+    f = lib.convrot_probe_stream
+    assert f(A, 12, A, None) == EINVAL                             # not a multiple of 8
+    assert f(A, -8, A, None) == EINVAL
+    assert f(None, 8, A, None) == EINVAL
+    assert f(A + 4, 8, A, None) == EALIGN
+    assert f(A, 8, A + 8, None) == EALIGN
+    assert f(None, 0, None, None) == 0                             # n = 0: nothing to do
+
+
 def test_variant_argument_errors(lib):
     F16 = 2
     # unknown io dtype / scale mode

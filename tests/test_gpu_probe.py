@@ -1,5 +1,6 @@
-"""The MFMA-rate probe (a measurement aid of the benchmark, not a step of the
-layer) really runs its int8 products on the operand bytes it is given.
+"""The measurement aids of the benchmark (not steps of the layer) do what they
+claim.  The MFMA-rate probe really runs its int8 products on the operand bytes
+it is given; the plain stream writes the high byte of every 16-bit value.
 
 Each lane of a wave holds four A and four B fragments of 16 bytes and the wave
 issues, per iteration, one 32x32x32 int8 MFMA for each of the 16 (A, B)
@@ -44,3 +45,14 @@ def test_probe_checksums(a_bytes, b_bytes, blocks, iters):
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.int64).reshape(blocks * 4, 64).sum(1)
     np.testing.assert_array_equal(got, expected_wave_sums(a, b, blocks, iters))
+
+
+@pytest.mark.parametrize("n", [8, 8000, 2048 * 256 * 8 * 3 + 24])
+def test_stream_probe_writes_high_bytes(n):
+    # the last size makes the 2048 workgroups loop three times and then some
+    import torch
+    from w8a8_rotated_int8_convrot_amd import binding
+    x = np.random.default_rng(n).integers(-32768, 32768, n, dtype=np.int64).astype(np.int16)
+    q = binding.convrot_probe_stream(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q.cpu().numpy(), (x >> 8).astype(np.int8))

@@ -39,6 +39,7 @@ SIGNATURES = {
     "convrot_gemm_i32": ([_P, _P, _I64, _I64, _I64, _P, _P], _I),
     "convrot_gemm_dequant": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _I),
     "convrot_probe_mfma_i8": ([_P, _I64, _P, _I64, _I, _I, _P, _P], _I),
+    "convrot_probe_stream": ([_P, _I64, _P, _P], _I),
     "convrot_prepare_weight_ex": ([_P, _I, _I64, _I64, _I, _I, _P, _P, _P, _SZ, _P], _I),
     "convrot_rotate_quant_ex": ([_P, _I, _I64, _I64, _I, _P, _P, _P], _I),
     "convrot_gemm_dequant_ex": ([_P, _P, _P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _P], _I),
@@ -207,6 +208,20 @@ def convrot_probe_mfma_i8(a, b, blocks, iters, out=None) -> torch.Tensor:
     _call("convrot_probe_mfma_i8", _ptr(a), a.numel(), _ptr(b), b.numel(), blocks, iters, _ptr(o),
           _stream(a))
     return o
+
+
+def convrot_probe_stream(x, out=None) -> torch.Tensor:
+    """Measurement aid: the traffic of rotate + quant without its arithmetic
+    (see include/convrot.h); x is a contiguous 16-bit CUDA tensor, returns the
+    int8 tensor of its high bytes, same shape."""
+    if x.dtype not in (torch.bfloat16, torch.float16, torch.int16) or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("convrot_probe_stream: x must be a contiguous 16-bit CUDA tensor")
+    q = torch.empty(x.shape, dtype=torch.int8, device=x.device) if out is None else out
+    _need(q, torch.int8, "out", x.dim())
+    if q.shape != x.shape:
+        raise ValueError("convrot_probe_stream: out shape mismatch")
+    _call("convrot_probe_stream", _ptr(x), x.numel(), _ptr(q), _stream(x))
+    return q
 
 
 def convrot_linear(x, wq, w_scale, group, bias=None, out=None, workspace=None) -> torch.Tensor:

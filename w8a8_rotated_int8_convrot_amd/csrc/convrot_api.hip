@@ -735,4 +735,16 @@ int convrot_probe_mfma_i8(const int8_t* a, int64_t a_bytes, const int8_t* b, int
                     who);
 }
 
+int convrot_probe_stream(const void* x_16, int64_t n, int8_t* q, void* stream) {
+  const char* who = "convrot_probe_stream";
+  if (n < 0 || n % 8 != 0) return fail(CONVROT_EINVAL, "%s: n = %lld must be a non-negative multiple of 8", who,
+                                       static_cast<long long>(n));
+  if (n > 0 && (!x_16 || !q)) return fail(CONVROT_EINVAL, "%s: NULL pointer", who);
+  if (n > 0 && (!aligned16(x_16) || !aligned16(q)))
+    return fail(CONVROT_EALIGN, "%s: x and q must be 16-byte aligned", who);
+  return hip_status(convrot::launch_stream_probe(static_cast<const uint16_t*>(x_16), n, q,
+                                                 static_cast<hipStream_t>(stream)),
+                    who);
+}
+
 }  // extern "C"

@@ -2,8 +2,8 @@
 // the C ABI).  Kernels live in rotate_quant.hip (rotation + quantization, and
 // the default path's weight unpacking), gemm_i8.hip (the int8 GEMM with its
 // epilogues, and the default path's bf16/fp16 product on the same tiles),
-// default_path.hip (the guarded layer's check) and mfma_probe.hip (a
-// measurement loop); argument checking, dispatch and the guard state live in
+// default_path.hip (the guarded layer's check) and mfma_probe.hip (two
+// measurement aids); argument checking, dispatch and the guard state live in
 // convrot_api.hip.
 #pragma once
 
@@ -93,5 +93,8 @@ __host__ __device__ inline int64_t sample_row(int i, int R, int64_t M) {
 // taken from a and b; one int32 per thread written to out.
 hipError_t launch_mfma_probe(const int8_t* a, int64_t a_bytes, const int8_t* b, int64_t b_bytes,
                              int blocks, int iters, int32_t* out, hipStream_t stream);
+// Plain stream (mfma_probe.hip): q[i] = high byte of x[i] for n 16-bit
+// values (n % 8 == 0, 16-byte aligned buffers).
+hipError_t launch_stream_probe(const uint16_t* x, int64_t n, int8_t* q, hipStream_t stream);
 
 }  // namespace convrot

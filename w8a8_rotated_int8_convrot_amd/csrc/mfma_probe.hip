@@ -1,6 +1,8 @@
-// mfma_probe.hip -- a measurement aid, not a step of the layer: the rate at
-// which this GPU sustains v_mfma_i32_32x32x32_i8 straight from registers, with
-// no memory traffic in the loop, on operand bytes the caller chooses.
+// mfma_probe.hip -- measurement aids, not steps of the layer.
+//
+// The MFMA loop: the rate at which this GPU sustains v_mfma_i32_32x32x32_i8
+// straight from registers, with no memory traffic in the loop, on operand
+// bytes the caller chooses.
 //
 // Under the board's power limit the shader clock, and with it this rate,
 // depends on how many operand bits toggle from one MFMA to the next: constant
@@ -51,7 +53,30 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(const int8_t* __restrict
   out[t] = s;
 }
 
+// The plain stream: the HBM traffic of rotate + quant (16-bit values in,
+// one byte per value out) with no arithmetic: each thread step loads eight
+// values (16 bytes) and stores their high bytes (8 bytes), grid-stride over
+// the buffer.  What it sustains is the practical bandwidth ceiling for that
+// traffic on this machine.
+__global__ __launch_bounds__(256) void stream_probe_kernel(const uint4* __restrict__ x, int64_t n8,
+                                                           uint2* __restrict__ q) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n8;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const uint4 w = x[i];
+    q[i] = make_uint2(__builtin_amdgcn_perm(w.y, w.x, 0x07050301u), __builtin_amdgcn_perm(w.w, w.z, 0x07050301u));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_stream_probe(const uint16_t* x, int64_t n, int8_t* q, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t n8 = n / 8;
+  const int64_t blocks = (n8 + 255) / 256 < 2048 ? (n8 + 255) / 256 : 2048;
+  hipLaunchKernelGGL(stream_probe_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
+                     reinterpret_cast<const uint4*>(x), n8, reinterpret_cast<uint2*>(q));
+  return hipGetLastError();
+}
 
 hipError_t launch_mfma_probe(const int8_t* a, int64_t a_bytes, const int8_t* b, int64_t b_bytes,
                              int blocks, int iters, int32_t* out, hipStream_t stream) {
