@@ -98,6 +98,13 @@ def test_gemm_stores_stay_inside_persistent_tiles(B, tile, M, N, K, monkeypatch)
     gemm_case(B, M, N, K, 11 * M + N)
 
 
+@pytest.mark.parametrize("tile", ["ksplit"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (13, 1001, 384), (16, 3001, 4096)])
+def test_gemm_stores_stay_inside_ksplit_tiles(B, tile, M, N, K, monkeypatch):
+    monkeypatch.setenv("CONVROT_GEMM_TILE", tile)
+    gemm_case(B, M, N, K, 13 * M + N)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (15, 12287, 512), (129, 3001, 384), (2001, 12283, 384)])
 def test_gemm_stores_stay_inside_automatic_tiles(B, M, N, K):
     # 2001 x 12283: whole rounds of 384 x 192 tiles, then ragged 384 x 96 tiles

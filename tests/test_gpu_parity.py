@@ -251,6 +251,30 @@ def test_small_and_ragged_shapes(B, M, N, K):
     assert np.all(same_bf16(bits_of(y), y_ref))
 
 
+# The few-token tiles (M <= 16): the one that splits K over its four waves
+# and the one-wave tile; K from one slab (three waves of the K-split tile
+# without work) to 96 slabs with uneven shares, ragged N, one token to
+# sixteen; int32 and the bf16 epilogue against the oracle.
+@pytest.mark.parametrize("tile", ["ksplit", "skinny16"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (7, 1000, 384), (16, 12289, 4096), (13, 3001, 12288),
+                                   (16, 64, 640), (2, 12288, 1152)])
+def test_few_token_tiles_bit_exact(B, tile, M, N, K, monkeypatch):
+    monkeypatch.setenv("CONVROT_GEMM_TILE", tile)
+    r = np.random.default_rng(M * N + K)
+    a = rand_i8((M, K), 3 * M + K)
+    b = rand_i8((N, K), 5 * N + K)
+    s_x = (r.random(M) * 0.2 + 1e-3).astype(np.float32)
+    s_w = np.float32(1.3e-4)
+    bias = synth.to_bf16_bits(r.standard_normal(N) * 0.01)
+    ad, bd = torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)
+    acc = B.convrot_gemm_i32(ad, bd).cpu().numpy()
+    y = B.convrot_gemm_dequant(ad, torch.from_numpy(s_x).to(DEV), bd, torch.tensor([s_w], device=DEV),
+                               to_dev_bf16(bias, DEV))
+    acc_ref = oracle.gemm_i32(a, b)
+    assert np.array_equal(acc, acc_ref)
+    assert np.all(same_bf16(bits_of(y), oracle.epilogue(acc_ref, s_x, s_w, bias)))
+
+
 def test_empty_batch_is_a_no_op(B):
     wq = torch.zeros((8, 128), dtype=torch.int8, device=DEV)
     s_w = torch.ones(1, device=DEV)

@@ -116,11 +116,13 @@ def test_linear_variants_end_to_end(io, mode, M, K, N, g):
     assert oracle.nrmse(widen(y_ref), ref) < 0.05
 
 
-@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "m32", "m64", "m128", "p128", "phalf", "tall", "ptall"])
+@pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "m32", "m64", "m128",
+                                  "p128", "phalf", "tall", "ptall", "ksplit"])
 def test_every_tile_runs_the_variant_epilogues(tile, monkeypatch):
     monkeypatch.setenv("CONVROT_GEMM_TILE", tile)
     r = np.random.default_rng(5)
-    M, N, K = 300, 1001, 384
+    # the K-split tiles hold at most 16 tokens
+    M, N, K = (13, 1001, 384) if tile == "ksplit" else (300, 1001, 384)
     a = r.integers(-127, 128, (M, K), dtype=np.int8)
     b = r.integers(-127, 128, (N, K), dtype=np.int8)
     s_x = (r.random(M) * 0.2 + 1e-3).astype(np.float32)

@@ -125,12 +125,13 @@ using TileMid = Tile<128, 128, 2, 2, 16, 4>;
 // rows, each with 15 slabs (30 KB) of loads in flight.
 using TileSkinny = Tile<32, 32, 1, 1, 32, 1, 16>;
 // M <= 16: 16 channels x 16 tokens per one-wave workgroup (16x16x64 MFMAs),
-// 24 stages of 2 KB, so that three workgroups share a CU: N = 12288 gives
-// 768 workgroups, exactly three per CU, with 22 slabs in flight each (a third
-// more weight bytes in flight per CU than the 32 x 32 tile, and no CU left
-// with a single workgroup).  With the weight read from HBM, 16 x 12288 x 4096
-// takes 13.0 us instead of 14.5, and 16 x 3072 x 12288 16.5 us instead of 27.
-using TileSkinny16 = Tile<16, 16, 1, 1, 16, 1, 24>;
+// eight stages of 128-byte slabs (4 KB: every direct-to-LDS load moves eight
+// whole 128-byte rows), so that three workgroups share a CU: N = 12288 gives
+// 768 workgroups, exactly three per CU.  With the weight read from HBM,
+// 16 x 3072 x 12288 takes 13.2 us (16.7 with 24 stages of 64-byte slabs, 12
+// stages of 128 bytes 14.2), 16 x 12288 x 4096 12.2 us (13.0; 12.6); with
+// many channels the K-split tile below is faster still.
+using TileSkinny16 = Tile<16, 16, 1, 1, 16, 1, 8, 128>;
 // 384 x 192 as TileWide, but 128-byte slabs in two stages: one barrier per
 // 128 bytes of K, and the direct-to-LDS loads fetch 128 contiguous bytes of
 // a row (eight lanes) per request instead of 64.  Tiles are walked in groups
@@ -520,12 +521,14 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
     static_assert(T::kKSteps <= 2, "three-plus stage pipeline runs one or two units per slab");
     wait_vm_barrier<(T::kStages - 2) * T::kLoads>();
     read_unit(0, 0, f0);
-    // K is a multiple of 128, so KT is even and the loop runs in slab pairs
-    // with fixed register roles.
+    // The loop runs in slab pairs with fixed register roles.  One unit per
+    // slab (64-byte slabs): K is a multiple of 128, so KT is even.  Two units
+    // per slab: every step leaves the next slab's first unit in f0, so an
+    // odd KT (128-byte slabs) just skips the last pair's second step.
     for (int kt = 0; kt < KT; kt += 2) {
       if constexpr (T::kKSteps == 2) {
         step(kt, f0, f1);       // f0 <- first unit of slab kt+1
-        step(kt + 1, f0, f1);
+        if (kt + 1 < KT) step(kt + 1, f0, f1);
       } else {
         step(kt, f0, f1);       // f1 <- slab kt+1
         step(kt + 1, f1, f0);
@@ -680,6 +683,168 @@ __global__ __launch_bounds__(T::kThreads) void gemm_i8_kernel(
       }
     }
   }
+}
+
+// ---------------------------------------------------------------- few tokens, K split over waves
+
+// The end of a K-split few-token tile: waves 1-3 park their 16 x 16 partial
+// sums in LDS, wave 0 adds them (integer sums: the result does not depend on
+// the split) and runs the epilogue.  Lane l holds channels n0 + 4 (l >> 4) + e
+// of token l & 15.
+template <int EPI, typename AccT>
+__device__ inline void ksplit_finish(AccT acc, v4i (&red)[3][64], int wave, int lane, int n0, int M, int N,
+                                     const float* __restrict__ x_scale, const float* __restrict__ w_scale,
+                                     const uint16_t* __restrict__ bias, void* __restrict__ out) {
+  constexpr bool DEQUANT = EPI != kEpiI32;
+  constexpr bool kRowScale = EPI == kEpiBf16Row || EPI == kEpiF16Row;
+  constexpr bool kDefault = EPI == kEpiDefBf16 || EPI == kEpiDefF16;
+  constexpr bool kF16 = EPI == kEpiF16 || EPI == kEpiF16Row || EPI == kEpiDefF16;
+  constexpr int OP = EPI == kEpiDefBf16 ? kOpBf16 : EPI == kEpiDefF16 ? kOpF16 : kOpI8;
+  if (wave > 0) red[wave - 1][lane] = __builtin_bit_cast(v4i, acc);
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    const v4i p = red[w][lane];
+    if constexpr (OP == kOpI8) acc += p;
+    else acc += __builtin_bit_cast(v4f, p);
+  }
+  const int m = lane & 15;
+  const int n = n0 + 4 * (lane >> 4);
+  if (m >= M) return;
+  if constexpr (!DEQUANT) {
+    int32_t* c = static_cast<int32_t*>(out) + static_cast<int64_t>(m) * N + n;
+    if ((N & 3) == 0 && n + 3 < N) {
+      *reinterpret_cast<int4*>(c) = make_int4(acc[0], acc[1], acc[2], acc[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) c[e] = acc[e];
+    }
+  } else {
+    float alpha = 0.0f;
+    if constexpr (!kDefault) alpha = kRowScale ? x_scale[m] : x_scale[m] * *w_scale;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ne = min(n + e, N - 1);
+      float b = 0.0f;
+      if (bias != nullptr)
+        b = kF16 ? static_cast<float>(__builtin_bit_cast(_Float16, bias[ne]))
+                 : __uint_as_float(static_cast<uint32_t>(bias[ne]) << 16);
+      if constexpr (kDefault) v[e] = acc[e] + b;
+      else if constexpr (kRowScale) v[e] = __builtin_fmaf(static_cast<float>(acc[e]), alpha * w_scale[ne], b);
+      else v[e] = __builtin_fmaf(static_cast<float>(acc[e]), alpha, b);
+    }
+    uint32_t w0, w1;
+    if constexpr (kF16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(v[e]));
+      w0 = pack_f16x2(v[0], v[1]);
+      w1 = pack_f16x2(v[2], v[3]);
+    } else {
+      w0 = pack_bf16x2(v[0], v[1]);
+      w1 = pack_bf16x2(v[2], v[3]);
+    }
+    uint16_t* y = static_cast<uint16_t*>(out) + static_cast<int64_t>(m) * N + n;
+    if ((N & 3) == 0 && n + 3 < N) {
+      *reinterpret_cast<uint2*>(y) = make_uint2(w0, w1);
+    } else {
+      const uint32_t ww[2] = {w0, w1};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) y[e] = static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
+// M <= 16: the weight stream is the whole cost, and a workgroup per 16 output
+// channels leaves one wave per workgroup to issue its loads.  Here the four
+// waves of a workgroup split K: wave w runs slabs [w KT / 4, (w + 1) KT / 4)
+// of 128 bytes (16 weight rows and the 16 token rows, 4 KB, four
+// direct-to-LDS loads of eight full 128-byte rows) through its own S-stage
+// ring in LDS, so the waves need no barrier until the end.  There waves 1-3
+// park their 16 x 16 int32 partial sums in LDS and wave 0 adds them (integer
+// sums: the result does not depend on the split) and runs the epilogue.
+// The default path's fp32 product takes the same route; its sum order then
+// differs from the other tiles' in the last bits, within its tolerance.
+// Two stages per wave (32 KB per workgroup, three per CU): weight from HBM,
+// 16 x 12288 x 4096 in 11.5 us against 12.2 with the one-wave tile (three
+// stages 11.9, four 16.1; loading the operands straight into registers,
+// 16 rows x 64 bytes per instruction, 17.4).  With N / 16 below twice the
+// CU count the one-wave tile is faster (16 x 3072 x 12288: 13.2 us against
+// 18.4): each wave's share of K is then too short.
+template <int EPI, int S>
+__global__ __launch_bounds__(256) void gemm_ksplit_kernel(
+    const int8_t* __restrict__ wq, const int8_t* __restrict__ xq, int M, int N, int K,
+    const float* __restrict__ x_scale, const float* __restrict__ w_scale, const uint16_t* __restrict__ bias,
+    void* __restrict__ out) {
+  constexpr bool DEQUANT = EPI != kEpiI32;
+  constexpr bool kRowScale = EPI == kEpiBf16Row || EPI == kEpiF16Row;
+  constexpr bool kDefault = EPI == kEpiDefBf16 || EPI == kEpiDefF16;
+  constexpr bool kF16 = EPI == kEpiF16 || EPI == kEpiF16Row || EPI == kEpiDefF16;
+  constexpr int OP = EPI == kEpiDefBf16 ? kOpBf16 : EPI == kEpiDefF16 ? kOpF16 : kOpI8;
+  constexpr int kStage = 4096;                      // A: 16 rows x 128 B, then B: 16 rows x 128 B
+  __shared__ __attribute__((aligned(16))) char lds[4 * S * kStage];
+  __shared__ __attribute__((aligned(16))) v4i red[3][64];
+  using acc_t = typename Acc<16, OP>::type;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * 16;
+  const int KT = K / 128;
+  const int kt0 = wave * KT / 4, nk = (wave + 1) * KT / 4 - kt0;
+  char* wl = lds + wave * S * kStage;
+  // a load fills eight 128-byte LDS rows: lane -> row 8 i + (lane >> 3),
+  // stored chunk lane & 7, fetched global chunk (lane & 7) ^ swz(row); rows
+  // past N or M read the last valid row (results discarded)
+  uint32_t off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 8 * (j & 1) + (lane >> 3);
+    const int c16 = ((lane & 7) ^ swz<16, 128>(row)) * 16;
+    off[j] = j < 2 ? static_cast<uint32_t>((min(n0 + row, N - 1) - n0) * K + c16)
+                   : static_cast<uint32_t>(min(row, M - 1) * K + c16);
+  }
+  const int8_t* a_tile = wq + static_cast<int64_t>(n0) * K;
+  auto issue = [&](int kt, int stage) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int8_t* base = (j < 2 ? a_tile : xq) + static_cast<int64_t>(kt) * 128;
+      asm volatile("" : "+v"(off[j]));
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off[j]),
+                                       (lds_void_t*)(wl + stage * kStage + (j >> 1) * 2048 + (j & 1) * 1024),
+                                       16, 0, 0);
+    }
+  };
+  // 16x16x64 fragment of unit kk (0, 1) of a slab: row lane & 15, chunk
+  // 4 kk + (lane >> 4)
+  const int frow = lane & 15;
+  int frag[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) frag[kk] = frow * 128 + (((4 * kk + (lane >> 4)) ^ swz<16, 128>(frow)) << 4);
+
+  acc_t acc = acc_t{};
+  if (nk > 0) {
+    // every step issues exactly one slab (past the end: the wave's last slab
+    // again, into the stage just finished, never read), so the wait count
+    // is fixed
+#pragma unroll
+    for (int s2 = 0; s2 < S - 1; ++s2) issue(kt0 + min(s2, nk - 1), s2);
+    for (int i = 0; i < nk; ++i) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * 4) : "memory");
+      issue(kt0 + min(i + S - 1, nk - 1), (i + S - 1) % S);
+      const char* st = wl + (i % S) * kStage;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const v4i a = *reinterpret_cast<const v4i*>(st + frag[kk]);
+        const v4i b = *reinterpret_cast<const v4i*>(st + 2048 + frag[kk]);
+        acc = mfma<16, OP>(a, b, acc);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  ksplit_finish<EPI>(acc, red, wave, lane, n0, M, N, x_scale, w_scale, bias, out);
 }
 
 // ---------------------------------------------------------------- persistent two-stage tiles
@@ -1174,6 +1339,17 @@ hipError_t launch_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
   return hipGetLastError();
 }
 
+// Few-token launch: 16 output channels per workgroup, K split over its four
+// waves (M <= 16).
+template <int EPI, int S>
+hipError_t launch_ksplit(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
+                         const uint16_t* bias, void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_ksplit_kernel<EPI, S>), dim3(static_cast<uint32_t>((N + 15) / 16)), dim3(256), 0,
+                     stream, wq, xq, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), x_scale,
+                     w_scale, bias, out);
+  return hipGetLastError();
+}
+
 // Persistent launch: one workgroup per CU (at most one per tile).
 template <class T, int EPI>
 hipError_t launch_persist(const int8_t* xq, const float* x_scale, const int8_t* wq,
@@ -1190,11 +1366,13 @@ hipError_t launch_persist(const int8_t* xq, const float* x_scale, const int8_t* 
   return hipGetLastError();
 }
 
-// Tile choice: CONVROT_GEMM_TILE=big|big8|wide|wide128|mid|skinny|skinny16|half|m32|m64|m128|p128|phalf|tall|ptall
+// Tile choice: CONVROT_GEMM_TILE=big|big8|wide|wide128|mid|skinny|skinny16|half|m32|m64|m128|p128|phalf|tall|ptall|ksplit
 // forces one (the result does not depend on it; p128, phalf and ptall are the
 // persistent 384 x 192, 384 x 96 and 192 x 288 kernels, which take the
-// one-tile kernel below three slabs of K).  Otherwise: M <= 16 streams
-// the weight with the 16 x 16 tile, and M <= 256 with the small tile whose
+// one-tile kernel below three slabs of K; ksplit holds at most 16 tokens).
+// Otherwise: M <= 16 streams the weight with the K-split 16 x 16 tile where
+// N / 16 is at least twice the CU count, else with the one-wave 16 x 16
+// tile, and M <= 256 with the small tile whose
 // slowest CU moves the fewest operand bytes; larger layers with fewer
 // 384 x 192 tiles than half the CUs use 384 x 96, 128 x 128 or 64 x 128
 // tiles; else the cost of a large tile is the number of rounds its tiles take
@@ -1218,6 +1396,7 @@ int forced_tile() {
   if (strcmp(e, "phalf") == 0) return 14;
   if (strcmp(e, "tall") == 0) return 15;
   if (strcmp(e, "ptall") == 0) return 16;
+  if (strcmp(e, "ksplit") == 0) return 19;
   return 0;
 }
 
@@ -1252,7 +1431,7 @@ int64_t wide_cost(int64_t M, int64_t N) {
 
 int pick_tile(int64_t M, int64_t N) {
   const int64_t kCUs = num_cus();
-  if (M <= 16) return 7;
+  if (M <= 16) return (N + 15) / 16 >= 2 * kCUs ? 19 : 7;
   if (M <= 256) {
     // Weight-streaming layers.  The slowest CU runs ceil(tiles / CUs) tiles,
     // each moving its BN weight rows and BM token rows per K byte; weight rows
@@ -1341,6 +1520,8 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
   if (t == 14) return launch_persist<TileWideHalf, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 15) return launch_tile<TileTall, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 16) return launch_persist<TileTall, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
+  if (t == 19 && M > 16) t = 7;   // the K-split tile holds 16 tokens
+  if (t == 19) return launch_ksplit<EPI, 2>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 7) return launch_tile<TileSkinny16, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 10) return launch_tile<TileM32, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
   if (t == 11) return launch_tile<TileM64, EPI>(xq, x_scale, wq, w_scale, bias, out, M, N, K, stream);
