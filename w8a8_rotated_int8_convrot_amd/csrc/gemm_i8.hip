@@ -7,10 +7,17 @@
 //   acc[m][n] = sum_k xq[m][k] * wq[n][k]                 (int32, exact)
 //   y[m][n]   = bf16_rne(fmaf((float)acc, x_scale[m] * w_scale, bias[n]))
 //
+// Kernels: gemm_i8_kernel (one tile per workgroup, any tile shape below),
+// gemm_persist_kernel (one workgroup per CU walking several 384 x 192 or
+// 192 x 288 tiles, its epilogue overlapped with the next tile's first MFMAs)
+// and gemm_ksplit_kernel (at most 16 tokens: the four waves of a workgroup
+// split K).  Which one runs is a performance choice (pick_tile): on the int8
+// path every one gives the same bytes (integer sums are exact in any order).
+//
 // Design for CDNA4:
-//  * v_mfma_i32_32x32x32_i8 (v_mfma_i32_16x16x64_i8 in the 8-wave and small
-//    tiles).  The weight tile is the instruction's A operand and the
-//    activation tile its B operand, so a lane's result block holds four
+//  * v_mfma_i32_32x32x32_i8 (v_mfma_i32_16x16x64_i8 in the 8-wave, 192 x 288
+//    and small tiles).  The weight tile is the instruction's A operand and
+//    the activation tile its B operand, so a lane's result block holds four
 //    consecutive output channels n of one token m.
 //  * Both operands are K-contiguous in HBM ([N, K] weight as stored by
 //    nn.Linear, [M, K] codes), so an A or B fragment is MF rows x 16
@@ -41,9 +48,11 @@
 //    one ds_read_b128 pass fall into distinct banks.  A lane's direct-to-LDS
 //    slot is fixed by its lane id, so the swizzle is applied by choosing
 //    which global chunk the lane fetches.
-//  * Epilogue: dequant + bias in registers, bf16 tile staged through LDS
-//    (chunk-XOR-swizzled rows), then written out as full contiguous rows with
-//    16-byte stores, so every output line leaves the CU whole.
+//  * Epilogue: dequant + bias in registers.  The one-tile kernel stages the
+//    bf16 tile through LDS (chunk-XOR-swizzled rows) and writes full
+//    contiguous rows with 16-byte stores; the persistent kernel stores
+//    straight from registers after a lane exchange (v_permlane32_swap or
+//    v_permlane16_swap) that gives each lane 16 contiguous bytes.
 //  * Tile order: the dispatcher places workgroup i on XCD i % 8, so the
 //    workgroup id is remapped to give each XCD a contiguous run of tiles, and
 //    runs are walked in groups of kGroupM token tiles so that neighbouring
