@@ -330,26 +330,18 @@ def stack_path(binding, synth, torch, dev, stream, g, reps=2):
     absmax drawn from U[5, 30]; the down projection reads the up projection's
     output.  The same stack runs on the int8 layer and on the default path
     (weight unpacked on every call, bf16 product), each timed with HIP events
-    over whole passes."""
+    over whole passes.  tests/test_gpu_stack.py checks blocks of this stack
+    against the oracle."""
     M = synth.STACK_M
-    gen = torch.Generator(device=dev)
     layers = []
     for b in range(synth.STACK_BLOCKS):
         for li, (kind, K, N) in enumerate(synth.STACK_LAYERS):
-            gen.manual_seed(0xC0517 + 5000 + 10 * (4 * b + li))
-            w = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
+            w, bias = synth.stack_weight_device(b, li, dev)
             wq, s_w = binding.convrot_prepare_weight(w, g)
-            bias = (torch.randn(N, generator=gen, device=dev) * 0.01).to(torch.bfloat16)
             layers.append((kind, wq, s_w, bias))
             del w
 
-    def tokens(seed):
-        gen.manual_seed(seed)
-        x = torch.randn((M, 3072), generator=gen, device=dev)
-        a = 5.0 + 25.0 * torch.rand((M, 1), generator=gen, device=dev)
-        return (x * (a / x.abs().amax(dim=1, keepdim=True))).to(torch.bfloat16)
-
-    x_in, x_attn = tokens(0xC0517 + 5001), tokens(0xC0517 + 5002)
+    x_in, x_attn = synth.stack_tokens_device(1, dev), synth.stack_tokens_device(2, dev)
     outs = {n: torch.empty((M, n), dtype=torch.bfloat16, device=dev) for n in (9216, 3072, 12288)}
     ws = torch.empty(max(binding.convrot_linear_workspace(M, K, N) for _, K, N in synth.STACK_LAYERS),
                      dtype=torch.uint8, device=dev)

@@ -217,6 +217,30 @@ def make_stack_layer(name: str, g: int = 128, M: int | None = None) -> Layer:
     return Layer(name, M, K, N, g, to_bf16_bits(x), _weight(5, layer, N, K), _bias(5, layer, N))
 
 
+def stack_weight_device(block: int, li: int, dev) -> tuple:
+    """The benchmark's device-drawn stack: layer li (index into STACK_LAYERS)
+    of block ``block``: fp32 weight N(0, 0.02^2) [N, K] and bf16 bias
+    N(0, 0.01^2) [N], from torch's generator on ``dev`` seeded per layer, so
+    that 6.79 GB of weights never pass through the host."""
+    _, K, N = STACK_LAYERS[li]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0xC0517 + 5000 + 10 * (4 * block + li))
+    w = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
+    bias = (torch.randn(N, generator=gen, device=dev) * 0.01).to(torch.bfloat16)
+    return w, bias
+
+
+def stack_tokens_device(which: int, dev):
+    """The stack's bf16 token rows [STACK_M, 3072] on ``dev`` (which = 1: the
+    block input, 2: the attention-output stand-in): N(0, 1) rows rescaled so
+    that each row's absmax is drawn from U[5, 30]."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0xC0517 + 5000 + which)
+    x = torch.randn((STACK_M, 3072), generator=gen, device=dev)
+    a = 5.0 + 25.0 * torch.rand((STACK_M, 1), generator=gen, device=dev)
+    return (x * (a / x.abs().amax(dim=1, keepdim=True))).to(torch.bfloat16)
+
+
 def sample_rows(M: int, count: int, seed: int) -> np.ndarray:
     """Sorted distinct token rows for sampled checks; always holds 0 and M-1."""
     r = np.argsort(uniform(seed, M), kind="stable")[:min(count, M)]
