@@ -292,7 +292,12 @@ int convrot_unpack_weight(const int8_t *wq, const float *w_scale, int scale_mode
 
 /* The default path for a whole batch: unpack the weight into the workspace
  * (convrot_default_workspace bytes), then y = rnd(x . Wu^T + bias).  Arguments
- * as convrot_linear_ex (x, bias and y in io_dtype); the same checks. */
+ * as convrot_linear_ex (x, bias and y in io_dtype); the same checks.  The
+ * product accumulates in fp32 on the matrix cores in an order that depends
+ * on the tile the shape takes (batches of at most 16 tokens with many
+ * channels split K over four waves), so y agrees with the exact value within
+ * one output ulp plus the fp32 bound of a K-term sum; a given shape repeats
+ * its bytes from call to call. */
 int convrot_default_linear(const void *x, int io_dtype, int64_t M, int64_t K, const int8_t *wq,
                            const float *w_scale, int scale_mode, int64_t N, int group,
                            const void *bias, void *y, void *workspace, size_t ws_bytes,
