@@ -421,6 +421,62 @@ def test_random_shapes_bit_exact(B, M, N, K):
     assert np.all(same_bf16(bits_of(y), oracle.epilogue(acc_ref, s_x, s_w, bias)))
 
 
+def _random_persistent(n, seed):
+    r = np.random.default_rng(seed)
+    return [(int(r.integers(1800, 6000)), int(r.integers(2000, 13000)), 128 * int(r.integers(3, 13)))
+            for _ in range(n)]
+
+
+# Seeded random shapes on the persistent kernels (several tiles per workgroup,
+# ragged in M and N, 3 to 12 slabs of K): int32 and the bf16 epilogue against
+# the oracle on seeded rows, which include the first and last.
+@pytest.mark.parametrize("tile", ["p128", "ptall"])
+@pytest.mark.parametrize("M,N,K", _random_persistent(6, 4242))
+def test_random_persistent_shapes_bit_exact(B, tile, M, N, K, monkeypatch):
+    monkeypatch.setenv("CONVROT_GEMM_TILE", tile)
+    a = rand_i8((M, K), 11 * M + K)
+    b = rand_i8((N, K), 13 * N + K)
+    r = np.random.default_rng(M * N + K)
+    s_x = (r.random(M) * 0.2 + 1e-3).astype(np.float32)
+    s_w = np.float32(1.2e-4)
+    bias = synth.to_bf16_bits(r.standard_normal(N) * 0.01)
+    ad, bd = torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)
+    acc = B.convrot_gemm_i32(ad, bd)
+    y = B.convrot_gemm_dequant(ad, torch.from_numpy(s_x).to(DEV), bd, torch.tensor([s_w], device=DEV),
+                               to_dev_bf16(bias, DEV))
+    rows = synth.sample_rows(M, 24, M + N)
+    ridx = torch.from_numpy(rows).to(DEV)
+    acc_ref = oracle.gemm_i32(a[rows], b)
+    assert np.array_equal(acc[ridx].cpu().numpy(), acc_ref)
+    assert np.all(same_bf16(bits_of(y[ridx]), oracle.epilogue(acc_ref, s_x[rows], s_w, bias)))
+
+
+def _random_few(n, seed):
+    r = np.random.default_rng(seed)
+    return [(int(r.integers(1, 17)), int(r.integers(8192, 16000)), 128 * int(r.integers(1, 40)))
+            for _ in range(n)]
+
+
+# Seeded random few-token shapes on the automatic choice, which is the K-split
+# tile for N / 16 >= 512 (every shape here): the whole int32 product and the
+# bf16 epilogue against the oracle.
+@pytest.mark.parametrize("M,N,K", _random_few(8, 1717))
+def test_random_few_token_shapes_bit_exact(B, M, N, K):
+    a = rand_i8((M, K), 17 * M + K)
+    b = rand_i8((N, K), 19 * N + K)
+    r = np.random.default_rng(M + N * K)
+    s_x = (r.random(M) * 0.2 + 1e-3).astype(np.float32)
+    s_w = np.float32(0.9e-4)
+    bias = synth.to_bf16_bits(r.standard_normal(N) * 0.01)
+    ad, bd = torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)
+    acc = B.convrot_gemm_i32(ad, bd).cpu().numpy()
+    y = B.convrot_gemm_dequant(ad, torch.from_numpy(s_x).to(DEV), bd, torch.tensor([s_w], device=DEV),
+                               to_dev_bf16(bias, DEV))
+    acc_ref = oracle.gemm_i32(a, b)
+    assert np.array_equal(acc, acc_ref)
+    assert np.all(same_bf16(bits_of(y), oracle.epilogue(acc_ref, s_x, s_w, bias)))
+
+
 def _random_rotq(n, seed):
     r = np.random.default_rng(seed)
     out = []

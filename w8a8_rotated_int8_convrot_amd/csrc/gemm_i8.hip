@@ -788,10 +788,6 @@ __global__ __launch_bounds__(256) void gemm_ksplit_kernel(
     const int8_t* __restrict__ wq, const int8_t* __restrict__ xq, int M, int N, int K,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale, const uint16_t* __restrict__ bias,
     void* __restrict__ out) {
-  constexpr bool DEQUANT = EPI != kEpiI32;
-  constexpr bool kRowScale = EPI == kEpiBf16Row || EPI == kEpiF16Row;
-  constexpr bool kDefault = EPI == kEpiDefBf16 || EPI == kEpiDefF16;
-  constexpr bool kF16 = EPI == kEpiF16 || EPI == kEpiF16Row || EPI == kEpiDefF16;
   constexpr int OP = EPI == kEpiDefBf16 ? kOpBf16 : EPI == kEpiDefF16 ? kOpF16 : kOpI8;
   constexpr int kStage = 4096;                      // A: 16 rows x 128 B, then B: 16 rows x 128 B
   __shared__ __attribute__((aligned(16))) char lds[4 * S * kStage];
