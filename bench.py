@@ -593,8 +593,9 @@ def main():
 
     # the matrix cores' own ceiling on this machine and this data: a
     # register-only MFMA loop fed with the layer's activation and weight codes
-    probe_blocks, probe_iters = 1024, 1400
-    probe_out = torch.empty(probe_blocks * 256, dtype=torch.int32, device=dev)
+    probe_blocks, probe_iters = 1024, 1000
+    probe_ops = probe_blocks * 12 * probe_iters * 16 * 32768
+    probe_out = torch.empty(probe_blocks * 768, dtype=torch.int32, device=dev)
     for _ in range(3):
         binding.convrot_probe_mfma_i8(q, wq, probe_blocks, probe_iters, out=probe_out)
     ev[0].record(stream)
@@ -603,7 +604,7 @@ def main():
     ev[1].record(stream)
     torch.cuda.synchronize()
     probe_ms = ev[0].elapsed_time(ev[1]) / 5
-    probe_tops = probe_blocks * 4 * probe_iters * 16 * 65536 / (probe_ms * 1e-3) / 1e12
+    probe_tops = probe_ops / (probe_ms * 1e-3) / 1e12
 
     # the same GEMM and the same register-only MFMA loop on constant codes
     # (every activation and weight byte 1): the board is power-limited, and
@@ -626,7 +627,7 @@ def main():
         binding.convrot_probe_mfma_i8(q1, wq1, probe_blocks, probe_iters, out=probe_out)
     ev[1].record(stream)
     torch.cuda.synchronize()
-    const_probe_tops = probe_blocks * 4 * probe_iters * 16 * 65536 / (ev[0].elapsed_time(ev[1]) / 5 * 1e-3) / 1e12
+    const_probe_tops = probe_ops / (ev[0].elapsed_time(ev[1]) / 5 * 1e-3) / 1e12
     # board power and GFX clock while the GEMM runs back to back, on the
     # workload's codes and on constant codes
     clk_work = clk_const = None
@@ -749,7 +750,7 @@ def main():
     }
     rq_bytes = 3 * M * K + 4 * M          # bf16 in, int8 codes + fp32 scales out
     out["mfma_ceiling"] = {
-        "kernel": "register-only v_mfma_i32_32x32x32_i8 loop (convrot_probe_mfma_i8) on this "
+        "kernel": "register-only v_mfma_i32_16x16x64_i8 loop at three waves per SIMD (convrot_probe_mfma_i8) on this "
                   "workload's activation and weight codes",
         "achieved": round(probe_tops, 1), "unit": "TOPS",
         "gemm_frac_of_ceiling": round(achieved / probe_tops, 4)}

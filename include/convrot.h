@@ -373,12 +373,12 @@ int convrot_guard_inject(int device, int fault);
  * benchmark can state the rate the matrix cores sustain on this machine,
  * under its power limit, for given operand bytes.
  *
- * Runs `blocks` workgroups of four waves (one per SIMD).  Every lane loads
- * four 16-byte fragments from a and four from b (a_bytes / 16 and
+ * Runs `blocks` workgroups of twelve waves (three per SIMD).  Every lane
+ * loads four 16-byte fragments from a and four from b (a_bytes / 16 and
  * b_bytes / 16 fragments are cycled through), then issues iters x 16
- * independent v_mfma_i32_32x32x32_i8 from registers, and writes one int32
- * checksum to out[blocks * 256].  Integer ops per call:
- * blocks * 4 * iters * 16 * 65536.  a, b and out are 16-byte aligned device
+ * independent v_mfma_i32_16x16x64_i8 from registers, and writes one int32
+ * checksum to out[blocks * 768].  Integer ops per call:
+ * blocks * 12 * iters * 16 * 32768.  a, b and out are 16-byte aligned device
  * buffers owned by the caller; asynchronous on `stream`.
  * Errors: NULL buffer, buffers under 16 bytes, blocks outside [1, 2^20] or
  * iters < 1 -> CONVROT_EINVAL; misalignment -> CONVROT_EALIGN; launch error

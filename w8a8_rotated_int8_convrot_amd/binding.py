@@ -198,13 +198,13 @@ def convrot_gemm_dequant(xq, x_scale, wq, w_scale, bias=None, out=None) -> torch
 def convrot_probe_mfma_i8(a, b, blocks, iters, out=None) -> torch.Tensor:
     """Measurement aid: register-only int8 MFMA loop on fragments of the int8
     tensors a and b (see include/convrot.h); returns the int32 checksums
-    [blocks * 256].  Integer ops: blocks * 4 * iters * 16 * 65536."""
+    [blocks * 768].  Integer ops: blocks * 12 * iters * 16 * 32768."""
     _need(a, torch.int8, "a", None)
     _need(b, torch.int8, "b", None)
-    o = torch.empty(blocks * 256, dtype=torch.int32, device=a.device) if out is None else out
+    o = torch.empty(blocks * 768, dtype=torch.int32, device=a.device) if out is None else out
     _need(o, torch.int32, "out", 1)
-    if o.numel() < blocks * 256:
-        raise ValueError("convrot_probe_mfma_i8: out needs blocks * 256 elements")
+    if o.numel() < blocks * 768:
+        raise ValueError("convrot_probe_mfma_i8: out needs blocks * 768 elements")
     _call("convrot_probe_mfma_i8", _ptr(a), a.numel(), _ptr(b), b.numel(), blocks, iters, _ptr(o),
           _stream(a))
     return o
