@@ -107,7 +107,9 @@ def test_gemm_stores_stay_inside_ksplit_tiles(B, tile, M, N, K, monkeypatch):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (15, 12287, 512), (129, 3001, 384), (2001, 12283, 384)])
 def test_gemm_stores_stay_inside_automatic_tiles(B, M, N, K):
-    # 2001 x 12283: whole rounds of 384 x 192 tiles, then ragged 384 x 96 tiles
+    # 2001 x 12283: ragged 192 x 288 tiles, some workgroups running two (the
+    # 384 x 192 tiles with their half-height tail are covered by the forced
+    # persistent tile "p128" above)
     gemm_case(B, M, N, K, 7 * M + N)
 
 

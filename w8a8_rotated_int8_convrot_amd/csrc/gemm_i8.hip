@@ -1471,7 +1471,14 @@ int pick_tile(int64_t M, int64_t N) {
   // 192 x 288 tiles where their rounds cost no more than those of 384 x 192
   // with its tail: with the epilogue run beside the next tile's first MFMAs
   // they are the faster of the two at equal cost (M = 4608, N = 12288,
-  // K = 3072: 140.4 us against 145.7; N = 3072 and 9216 take fewer rounds)
+  // K = 3072: 140.4 us against 145.7; N = 3072 and 9216 take fewer rounds).
+  // Where 384 x 192 would need its half-height tail, 192 x 288 tiles are
+  // taken at any cost: the tail is a launch of its own whose 384 x 96 tiles
+  // run one per workgroup with nothing beside their prologue and epilogue,
+  // and it lost on every shape measured (4700 x 12290 x 640: 67 us with
+  // 192 x 288 against 80; 16896 x 9216 x 3072: 404 against 427;
+  // 19894 x 4096 x 384: 55 against 68).
+  if (wide_main_m(M, N) < (M + 191) / 192) return 16;
   if (tile_cost(M, N, 192, 288) <= wide_cost(M, N)) return 16;
   // the 256 x 256 tile (one wave per SIMD) wins only by a clear margin: it
   // was as fast or slower on every shape measured, also where its cost is
