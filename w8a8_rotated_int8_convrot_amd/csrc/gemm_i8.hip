@@ -27,11 +27,14 @@
 //  * Global -> LDS by direct-to-LDS loads (global_load_lds_dwordx4: each
 //    wave instruction fills 1 KB of LDS rows, no registers involved).  A
 //    "slab" is BK bytes of K of both operand tiles.  Two pipelines:
-//    - BK = 128, two stages (the default 384 x 192 tile): the slab after
-//      next is issued at each slab boundary into the stage just finished; a
-//      row's 128 bytes are one request, which halves the L1 -> L2 request
-//      count of 64-byte slabs, and there is one barrier per 128 bytes of K;
-//    - BK = 64, three or more stages, prefetched kStages-1 slabs ahead.
+//    - BK = 128, two stages (the 192 x 288, 384 x 192 and 384 x 96 tiles):
+//      the slab after next is issued at each slab boundary into the stage
+//      just finished; a row's 128 bytes are one request, which halves the
+//      L1 -> L2 request count of 64-byte slabs, and there is one barrier per
+//      128 bytes of K;
+//    - BK = 64 or 128, three or more stages, prefetched kStages-1 slabs
+//      ahead (the other tiles; the K-split kernel gives each wave its own
+//      two-stage ring).
 //    Fragments are double-buffered per MFMA k step: while one k step's MFMAs
 //    run from one register set, the LDS reads of the next fill the other.
 //    A load's address is a scalar base (the tile's first operand row plus the
@@ -1380,9 +1383,10 @@ hipError_t launch_persist(const int8_t* xq, const float* x_scale, const int8_t* 
 // tile, and M <= 256 with the small tile whose
 // slowest CU moves the fewest operand bytes; larger layers with fewer
 // 384 x 192 tiles than half the CUs use 384 x 96, 128 x 128 or 64 x 128
-// tiles; else the cost of a large tile is the number of rounds its tiles take
-// over the 256 CUs times the work of one tile, and the cheaper of 256x256 and
-// 384x192 (with its half-height tail, below) wins.
+// tiles.  Else the cost of a large tile is the number of rounds its tiles
+// take over the CUs times the work of one tile: 192 x 288 wherever 384 x 192
+// would need its half-height tail or costs no less, then the cheaper of
+// 384 x 192 and 256 x 256 (the latter only by a clear margin).
 int forced_tile() {
   const char* e = getenv("CONVROT_GEMM_TILE");
   if (e == nullptr) return 0;
