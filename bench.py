@@ -17,10 +17,11 @@ Printed: one JSON line with the metric (int8 TOPS = 2*M*N*K / step time), the
 roofline of the dominant kernel (the GEMM, timed with HIP events on the stream
 it runs on over K back-to-back launches right after the timed steps) and the
 CPU oracle timed on a bounded sample of token rows.  Beside them:
-  mfma_ceiling  the rate a register-only MFMA loop sustains on this machine
-                with this workload's own int8 codes (the board's power limit
-                lowers the clock with operand toggling), and the GEMM's
-                fraction of it; power_check adds the board power and GFX
+  mfma_ceiling  the rate a register-only MFMA loop in the GEMM's own form
+                (v_mfma_i32_16x16x64_i8, three waves per SIMD) sustains on
+                this machine with this workload's own int8 codes (the board's
+                power limit lowers the clock with operand toggling), and the
+                GEMM's fraction of it; power_check adds the board power and GFX
                 clock read with amd-smi while the GEMM runs back to back on
                 the workload's codes and on constant codes, and the int8 peak
                 scaled to the clock the workload's codes sustain;
@@ -33,10 +34,13 @@ CPU oracle timed on a bounded sample of token rows.  Beside them:
                 int8 weight to bf16, then the bf16 product -- beside the
                 int8 layer; the guarded layer once its check has run; and
                 one synthetic DiT denoising step's 240-layer linear stack on
-                both paths (the analogue of the pages' per-step timings); the
-                whole layer on the other workload shapes (tiny, QKV, MLP down,
-                2048^2 MLP up); and single steps, each timed alone, with and
-                without a 512 MB write before it (median and minimum).
+                both paths (the analogue of the pages' per-step timings);
+                eight layers with their int8 weights streamed from pinned
+                host memory; the whole layer on the other workload shapes
+                (tiny, QKV, MLP down, 2048^2 MLP up) and the MLP pair as a
+                chain (up, GELU-tanh, down) with its error against the fp64
+                chain; and single steps, each timed alone, with and without a
+                512 MB write before it (median and minimum).
 """
 import argparse
 import hashlib
