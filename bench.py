@@ -262,7 +262,7 @@ def small_m_paths(binding, synth, np, torch, dev, stream, g, steps):
     lin_bytes = gemm_bytes + 3 * M * K + 4 * M
     wl = f"M={M} tokens, K={K}, N={N}, group {g}, weight read from HBM (8 rotating copies)"
     return {
-        "small_m_gemm": {"kernel": "gemm_ksplit_kernel (16x16 tile, K split over its four waves)", "workload": wl, "bound": "hbm",
+        "small_m_gemm": {"kernel": "gemm_ksplit_reg_kernel (16x16 tile, K split over its four waves, operands streamed through registers)", "workload": wl, "bound": "hbm",
                          "ms": round(gemm_ms, 5), "bytes": gemm_bytes,
                          "achieved": round(gemm_bytes / (gemm_ms * 1e-3) / 1e9, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -107,10 +107,12 @@ def test_default_linear_within_bound(io, mode, M, N, K):
 
 
 @pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "half", "p128", "phalf", "tall", "ptall",
-                                  "m32", "m64", "m128", "ksplit"])
+                                  "m32", "m64", "m128", "ksplit", "ksplit1536", "ksplit2048"])
 def test_default_product_on_every_tile(tile, monkeypatch):
-    monkeypatch.setenv("CONVROT_GEMM_TILE", tile)
-    M, N, K, g = (11, 1001, 640, 128) if tile == "ksplit" else (300, 1001, 640, 128)
+    monkeypatch.setenv("CONVROT_GEMM_TILE", tile[:6] if tile.startswith("ksplit") else tile)
+    # the bf16 product runs the tiles with K counted in bytes: K = 1536 and
+    # 2048 elements take the K-split tile's register-streamed form
+    M, N, K, g = (11, 1001, int(tile[6:] or 640), 128) if tile.startswith("ksplit") else (300, 1001, 640, 128)
     wq, s_w = prepared(N, K, g, "tensor", 5)
     x = act(M, K, 6, "bf16")
     y = B.convrot_default_linear(dev16(x, "bf16"), wq, s_w, g, None)

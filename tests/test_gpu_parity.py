@@ -254,10 +254,12 @@ def test_small_and_ragged_shapes(B, M, N, K):
 # The few-token tiles (M <= 16): the one that splits K over its four waves
 # and the one-wave tile; K from one slab (three waves of the K-split tile
 # without work) to 96 slabs with uneven shares, ragged N, one token to
-# sixteen; int32 and the bf16 epilogue against the oracle.
+# sixteen, and K = 3072 and 4096, where the K-split tile streams its operands
+# through registers; int32 and the bf16 epilogue against the oracle.
 @pytest.mark.parametrize("tile", ["ksplit", "skinny16"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (7, 1000, 384), (16, 12289, 4096), (13, 3001, 12288),
-                                   (16, 64, 640), (2, 12288, 1152)])
+                                   (16, 64, 640), (2, 12288, 1152), (5, 12290, 3072), (16, 33, 4096),
+                                   (1, 17, 3072)])
 def test_few_token_tiles_bit_exact(B, tile, M, N, K, monkeypatch):
     monkeypatch.setenv("CONVROT_GEMM_TILE", tile)
     r = np.random.default_rng(M * N + K)

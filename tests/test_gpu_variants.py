@@ -117,12 +117,13 @@ def test_linear_variants_end_to_end(io, mode, M, K, N, g):
 
 
 @pytest.mark.parametrize("tile", ["big", "big8", "wide", "wide128", "mid", "skinny", "skinny16", "m32", "m64", "m128",
-                                  "p128", "phalf", "tall", "ptall", "ksplit"])
+                                  "p128", "phalf", "tall", "ptall", "ksplit", "ksplit3072", "ksplit4096"])
 def test_every_tile_runs_the_variant_epilogues(tile, monkeypatch):
-    monkeypatch.setenv("CONVROT_GEMM_TILE", tile)
+    monkeypatch.setenv("CONVROT_GEMM_TILE", tile[:6] if tile.startswith("ksplit") else tile)
     r = np.random.default_rng(5)
-    # the K-split tiles hold at most 16 tokens
-    M, N, K = (13, 1001, 384) if tile == "ksplit" else (300, 1001, 384)
+    # the K-split tiles hold at most 16 tokens; at K = 3072 and 4096 the
+    # K-split tile streams its operands through registers
+    M, N, K = (13, 1001, int(tile[6:] or 384)) if tile.startswith("ksplit") else (300, 1001, 384)
     a = r.integers(-127, 128, (M, K), dtype=np.int8)
     b = r.integers(-127, 128, (N, K), dtype=np.int8)
     s_x = (r.random(M) * 0.2 + 1e-3).astype(np.float32)

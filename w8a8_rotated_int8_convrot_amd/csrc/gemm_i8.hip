@@ -10,8 +10,9 @@
 // Kernels: gemm_i8_kernel (one tile per workgroup, any tile shape below),
 // gemm_persist_kernel (one workgroup per CU walking several 384 x 192 or
 // 192 x 288 tiles, its epilogue overlapped with the next tile's first MFMAs)
-// and gemm_ksplit_kernel (at most 16 tokens: the four waves of a workgroup
-// split K).  Which one runs is a performance choice (pick_tile): on the int8
+// and gemm_ksplit_kernel / gemm_ksplit_reg_kernel (at most 16 tokens: the
+// four waves of a workgroup split K; the second streams the operands through
+// registers, for K = 3072 and 4096).  Which one runs is a performance choice (pick_tile): on the int8
 // path every one gives the same bytes (integer sums are exact in any order).
 //
 // Design for CDNA4:
@@ -855,6 +856,84 @@ __global__ __launch_bounds__(256) void gemm_ksplit_kernel(
   ksplit_finish<EPI>(acc, red, wave, lane, n0, M, N, x_scale, w_scale, bias, out);
 }
 
+// The same K split for K = 512 NK (each wave NK slabs: K = 3072 and 4096),
+// with the operands streamed through registers: a lane loads 16 bytes of a
+// 128-byte row piece (eight lanes per row, eight rows per load, whole cache
+// lines), four slabs ahead, and writes each slab into a wave-private
+// two-stage LDS ring in the MFMA layout, from which the fragments are read as
+// in the kernel above.  A timing probe of the two weight paths alone (768
+// workgroups of four waves, 50 MB from HBM) gave 10.1-10.5 us through
+// direct-to-LDS rings of any depth and 6.9-7.3 us through registers with four
+// to eight slabs in flight.  The steps are unrolled, so the compiler's wait
+// counts stay exact (in a rolled loop they fell back to waiting for every
+// load at each pass).  16 x 12288 x 4096: 10.7-10.8 us instead of 11.4-11.5;
+// 16 x 12288 x 3072: 8.7-8.8 instead of 9.4.
+template <int EPI, int NK>
+__global__ __launch_bounds__(256) void gemm_ksplit_reg_kernel(
+    const int8_t* __restrict__ wq, const int8_t* __restrict__ xq, int M, int N, int K,
+    const float* __restrict__ x_scale, const float* __restrict__ w_scale, const uint16_t* __restrict__ bias,
+    void* __restrict__ out) {
+  constexpr int OP = EPI == kEpiDefBf16 ? kOpBf16 : EPI == kEpiDefF16 ? kOpF16 : kOpI8;
+  constexpr int kStage = 4096;                      // A: 16 rows x 128 B, then B: 16 rows x 128 B
+  constexpr int kAhead = 4;                         // slabs in flight per wave
+  __shared__ __attribute__((aligned(16))) char lds[4 * 2 * kStage];
+  __shared__ __attribute__((aligned(16))) v4i red[3][64];
+  using acc_t = typename Acc<16, OP>::type;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * 16;
+  const int kt0 = wave * NK;
+  char* wl = lds + wave * 2 * kStage;
+  // a slab is four 16-byte loads per lane: j = 0, 1 the weight rows
+  // 8 j + (lane >> 3), j = 2, 3 the token rows 8 (j - 2) + (lane >> 3), chunk
+  // lane & 7 of the slab's 128 bytes; rows past N or M read the last valid
+  // row (results discarded).  In LDS the chunk goes to slot
+  // (lane & 7) ^ swz(row), the layout the direct-to-LDS loads above produce.
+  uint32_t goff[4];
+  int loff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 8 * (j & 1) + (lane >> 3);
+    const int c16 = (lane & 7) * 16;
+    goff[j] = j < 2 ? static_cast<uint32_t>((min(n0 + row, N - 1) - n0) * K + c16)
+                    : static_cast<uint32_t>(min(row, M - 1) * K + c16);
+    loff[j] = (j >> 1) * 2048 + row * 128 + (((lane & 7) ^ swz<16, 128>(row)) << 4);
+  }
+  const int8_t* a_tile = wq + static_cast<int64_t>(n0) * K;
+  v4i buf[kAhead][4];
+  auto load = [&](int kt, v4i (&r)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      r[j] = *reinterpret_cast<const v4i*>((j < 2 ? a_tile : xq) + static_cast<int64_t>(kt) * 128 + goff[j]);
+  };
+  const int frow = lane & 15;
+  int frag[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) frag[kk] = frow * 128 + (((4 * kk + (lane >> 4)) ^ swz<16, 128>(frow)) << 4);
+
+  acc_t acc = acc_t{};
+#pragma unroll
+  for (int d = 0; d < kAhead && d < NK; ++d) load(kt0 + d, buf[d]);
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    char* st = wl + (i & 1) * kStage;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(st + loff[j]) = buf[i % kAhead][j];
+    if (i + kAhead < NK) load(kt0 + i + kAhead, buf[i % kAhead]);
+    // the wave reads what its own lanes just wrote (and wrote over what it
+    // read two slabs ago): a wave's LDS accesses complete in order
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const v4i a = *reinterpret_cast<const v4i*>(st + frag[kk]);
+      const v4i b = *reinterpret_cast<const v4i*>(st + 2048 + frag[kk]);
+      acc = mfma<16, OP>(a, b, acc);
+    }
+  }
+  ksplit_finish<EPI>(acc, red, wave, lane, n0, M, N, x_scale, w_scale, bias, out);
+}
+
 // ---------------------------------------------------------------- persistent two-stage tiles
 //
 // One workgroup per CU walks its share of the tiles (the same XCD-aware order
@@ -1348,13 +1427,21 @@ hipError_t launch_tile(const int8_t* xq, const float* x_scale, const int8_t* wq,
 }
 
 // Few-token launch: 16 output channels per workgroup, K split over its four
-// waves (M <= 16).
+// waves (M <= 16); the register-streamed kernel where K = 3072 or 4096.
 template <int EPI, int S>
 hipError_t launch_ksplit(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
                          const uint16_t* bias, void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_ksplit_kernel<EPI, S>), dim3(static_cast<uint32_t>((N + 15) / 16)), dim3(256), 0,
-                     stream, wq, xq, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), x_scale,
-                     w_scale, bias, out);
+  const dim3 grid(static_cast<uint32_t>((N + 15) / 16));
+  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  if (K == 512 * 8)
+    hipLaunchKernelGGL((gemm_ksplit_reg_kernel<EPI, 8>), grid, dim3(256), 0, stream, wq, xq, m, n, k, x_scale,
+                       w_scale, bias, out);
+  else if (K == 512 * 6)
+    hipLaunchKernelGGL((gemm_ksplit_reg_kernel<EPI, 6>), grid, dim3(256), 0, stream, wq, xq, m, n, k, x_scale,
+                       w_scale, bias, out);
+  else
+    hipLaunchKernelGGL((gemm_ksplit_kernel<EPI, S>), grid, dim3(256), 0, stream, wq, xq, m, n, k, x_scale, w_scale,
+                       bias, out);
   return hipGetLastError();
 }
 
