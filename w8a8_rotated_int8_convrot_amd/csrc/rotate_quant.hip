@@ -299,7 +299,7 @@ __device__ inline void dpp_fmac8(float (&v)[64], float sgn) {
 
 template <int G, typename In16>
 __global__ __launch_bounds__(512) void rotq_block_kernel(
-    const In16* __restrict__ x, int64_t M, int K, int rows_per_wg,
+    const In16* __restrict__ x, int64_t M, int K, int rows_per_wg, uint32_t bpr_inv,
     int8_t* __restrict__ q, float* __restrict__ scale) {
   // the input tile, 256 bytes per block of the workgroup (sized at launch)
   extern __shared__ __attribute__((aligned(16))) uint4 tile[];
@@ -322,20 +322,37 @@ __global__ __launch_bounds__(512) void rotq_block_kernel(
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     loff[r] = static_cast<uint32_t>(((lane >> 4) * 16 + ((lane & 15) ^ ((4 * r + (lane >> 4)) & 15))) * 16);
+  if (wchunks == 512) {
+    // a whole wave: eight unconditional loads, each a scalar base (kept
+    // opaque, so that it stays in scalar registers) plus the lane's offset
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    if (u * 64 >= wchunks) break;
-    if (64 * u + lane < wchunks) {
+    for (int u = 0; u < 8; ++u) {
       asm volatile("" : "+v"(loff[u & 3]));
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(wbase + u * 1024 + loff[u & 3]),
+      const char* base = wbase + u * 1024;
+      asm volatile("" : "+s"(base));
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + loff[u & 3]),
                                        (__attribute__((address_space(3))) void*)(tile + 512 * wave + 64 * u), 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u * 64 >= wchunks) break;
+      if (64 * u + lane < wchunks) {
+        asm volatile("" : "+v"(loff[u & 3]));
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(wbase + u * 1024 + loff[u & 3]),
+                                         (__attribute__((address_space(3))) void*)(tile + 512 * wave + 64 * u), 16, 0, 0);
+      }
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const int b = tid >> 1, half = tid & 1;
   const bool active = b < nblk;
-  const int lrow = active ? b / bpr : 0;
+  // b / bpr as (b * bpr_inv) >> 16 with bpr_inv = ceil(2^16 / bpr), exact
+  // for b < 256 and bpr <= 256 (checked for every pair), instead of an
+  // integer division
+  const int lrow = active ? static_cast<int>(__umul24(static_cast<uint32_t>(b), bpr_inv) >> 16) : 0;
+  const bool row_first = b == lrow * bpr;
   float v[64];
   float amax = 0.0f;
   // the normalisation constant times the sign this lane's values carry
@@ -396,7 +413,7 @@ __global__ __launch_bounds__(512) void rotq_block_kernel(
   uint4* codes = tile;
   if (active) {
     const float s = __uint_as_float(row_amax[lrow]) / 127.0f;
-    if (b % bpr == 0 && half == 0) scale[row0 + lrow] = s;
+    if (row_first && half == 0) scale[row0 + lrow] = s;
     const float r = 1.0f / s;
     char* out = reinterpret_cast<char*>(codes) + b * 128;
     if (r < 1e30f) {
@@ -440,9 +457,20 @@ __global__ __launch_bounds__(512) void rotq_block_kernel(
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   uint4* dstq = reinterpret_cast<uint4*>(q + row0 * K);
   const int wcodes = wchunks / 2;
-  for (int cc = 256 * wave + lane; cc < 256 * wave + wcodes; cc += 64) {
-    const int bb = cc >> 3, j = cc & 7;
-    dstq[cc] = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(codes) + bb * 128)[j ^ ((bb >> 1) & 7)];
+  if (wcodes == 256) {
+    // a whole wave: piece i of lane l is chunk l & 7 of block
+    // 32 wave + (l >> 3) + 8 i, stored at chunk (l & 7) ^ (l >> 4) for even
+    // i and ^ (l >> 4) ^ 4 for odd i: two lane offsets and immediates
+    const char* cb = reinterpret_cast<const char*>(codes);
+    const int o = (32 * wave + (lane >> 3)) * 128 + (((lane & 7) ^ (lane >> 4)) << 4);
+    uint4* d = dstq + 256 * wave + lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[64 * i] = *reinterpret_cast<const uint4*>(cb + (o ^ (64 * (i & 1))) + 1024 * i);
+  } else {
+    for (int cc = 256 * wave + lane; cc < 256 * wave + wcodes; cc += 64) {
+      const int bb = cc >> 3, j = cc & 7;
+      dstq[cc] = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(codes) + bb * 128)[j ^ ((bb >> 1) & 7)];
+    }
   }
 }
 
@@ -611,12 +639,14 @@ hipError_t rotate_quant_16(const In16* x, int64_t M, int64_t K, int group, int8_
     const int blocks = rows_per_wg * static_cast<int>(K / kBlockElems);
     const int threads = (2 * blocks + 63) / 64 * 64;
     const size_t lds = static_cast<size_t>(blocks) * 256;
+    const uint32_t bpr = static_cast<uint32_t>(K / kBlockElems);
+    const uint32_t bpr_inv = (65536u + bpr - 1u) / bpr;
     if (group == 128)
       hipLaunchKernelGGL((rotq_block_kernel<128, In16>), dim3(static_cast<uint32_t>(wgs)), dim3(threads), lds,
-                         stream, x, M, static_cast<int>(K), rows_per_wg, q, scale);
+                         stream, x, M, static_cast<int>(K), rows_per_wg, bpr_inv, q, scale);
     else
       hipLaunchKernelGGL((rotq_block_kernel<256, In16>), dim3(static_cast<uint32_t>(wgs)), dim3(threads), lds,
-                         stream, x, M, static_cast<int>(K), rows_per_wg, q, scale);
+                         stream, x, M, static_cast<int>(K), rows_per_wg, bpr_inv, q, scale);
     return hipGetLastError();
   }
   return dispatch_group<In16, kActQuant>(group, x, M, K, q, scale, nullptr, stream);
