@@ -86,6 +86,15 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
+_T0 = time.perf_counter()
+
+
+def progress(msg):
+    """One line on stderr as each part of the run ends (the JSON line stays
+    alone on stdout)."""
+    print(f"bench.py: {msg} ({time.perf_counter() - _T0:.1f} s)", file=sys.stderr, flush=True)
+
+
 def gemm_source_hash():
     h = hashlib.sha256()
     for p in GEMM_SOURCES:
@@ -564,6 +573,7 @@ def main():
             break
     settle_s = time.perf_counter() - settle_t0
     step_s, step_ms_events = warm_and_time()
+    progress(f"settled and timed {args.steps} steps")
 
     # the dominant kernel (GEMM + epilogue) on its own: K back-to-back launches
     # on the same stream between one pair of HIP events, so the per-launch time
@@ -609,6 +619,7 @@ def main():
     torch.cuda.synchronize()
     probe_ms = ev[0].elapsed_time(ev[1]) / 5
     probe_tops = probe_ops / (probe_ms * 1e-3) / 1e12
+    progress("GEMM, rotate+quant, stream and MFMA-loop ceilings timed")
 
     # the same GEMM and the same register-only MFMA loop on constant codes
     # (every activation and weight byte 1): the board is power-limited, and
@@ -642,10 +653,15 @@ def main():
                                       const_gemm_ms, args.clock_seconds)
     del q1, wq1
 
+    progress("constant-code runs and clocks done")
     small = small_m_paths(binding, synth, np, torch, dev, stream, g, args.steps)
+    progress("few-token paths done")
     streamed = streamed_path(binding, torch, dev, stream, x, wq, s_w, g, bias)
+    progress("streamed weights done")
     stack = stack_path(binding, synth, torch, dev, stream, g)
+    progress("DiT step stack done")
     configs = configs_path(binding, synth, np, torch, dev, stream, g)
+    progress("other workload shapes and the MLP pair done")
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     single = {"unflushed": per_step_times(torch, stream, step, 20),
               "flushed": per_step_times(torch, stream, step, 20, flush=flush_buf)}
@@ -715,6 +731,7 @@ def main():
                           args.steps)
     binding.convrot_guard_reset(0)
     del ws_def, wu, ws_g
+    progress("variants, default path and guarded layer done")
 
     ops = 2.0 * M * N * K
     ops_total = ops
@@ -807,6 +824,7 @@ def main():
     }
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
+        progress("oracle timed on the host")
     print(json.dumps(out), flush=True)
 
 
