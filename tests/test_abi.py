@@ -268,3 +268,16 @@ def test_guard_state_on_the_host(lib, binding):
     with pytest.raises(ValueError):
         binding.convrot_guard_inject(0, "segfault")
     assert ctypes.sizeof(binding.GuardInfo) == 288
+
+
+def test_token_row_multiply_shift_is_exact():
+    """The token-block rotate kernel finds a lane's token row as
+    (b * ceil(2^16 / bpr)) >> 16 instead of b / bpr, for block index
+    b < 256 (two lanes per block, at most 512 lanes) and bpr = K / 128 <= 256
+    blocks per row (K <= 32768 on that kernel).  Exact for every such pair,
+    and every product fits the 24-bit multiplier it uses."""
+    for bpr in range(1, 257):
+        inv = (65536 + bpr - 1) // bpr
+        for b in range(256):
+            assert b * inv < (1 << 24)
+            assert (b * inv) >> 16 == b // bpr, (b, bpr)
